@@ -357,7 +357,10 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
     if (threadIdx.x == 0) atomicOr(flag, FLAG_TARGET);
     y = y < 0 ? 0 : vt - 1;
   }
-  float zy = to_f(z[y]);
+  // The target logit is taken from the registers of the thread that loaded
+  // it (a separate global read could still be in flight when another wave
+  // overwrites the row with the gradient).
+  __shared__ float sh_zy;
   uint4 buf[NCH];
   float mx = -INFINITY;
 #pragma unroll
@@ -366,11 +369,15 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
     if (e0 < V) {
       buf[k] = *(const uint4*)(z + e0);
 #pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e0 + j < V) mx = fmaxf(mx, chunk_elem<T>(buf[k], j));
+      for (int j = 0; j < E; ++j) {
+        float v = chunk_elem<T>(buf[k], j);
+        if (e0 + j < V) mx = fmaxf(mx, v);
+        if (e0 + j == y) sh_zy = v;
+      }
     }
   }
   mx = block_reduce_max(mx, sh);
+  const float zy = sh_zy;
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
@@ -421,10 +428,15 @@ __global__ __launch_bounds__(256) void k_xent_stream(T* __restrict__ logits, int
     if (threadIdx.x == 0) atomicOr(flag, FLAG_TARGET);
     y = y < 0 ? 0 : vt - 1;
   }
-  float zy = to_f(z[y]);
+  __shared__ float sh_zy;
   float mx = -INFINITY;
-  for (int e = threadIdx.x; e < V; e += 256) mx = fmaxf(mx, to_f(z[e]));
+  for (int e = threadIdx.x; e < V; e += 256) {
+    float v = to_f(z[e]);
+    mx = fmaxf(mx, v);
+    if (e == y) sh_zy = v;
+  }
   mx = block_reduce_max(mx, sh);
+  const float zy = sh_zy;
   float s = 0.f;
   for (int e = threadIdx.x; e < V; e += 256)
     s += __builtin_amdgcn_exp2f((to_f(z[e]) - mx) * LOG2E);

@@ -612,6 +612,9 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
   if ((e = hipMemsetAsync(c->av, 0, c->nflat * 4, c->st))) return bail(e, "zero v");
   if ((e = hipMemsetAsync(c->scal, 0, 64 * 4, c->st))) return bail(e, "zero scalars");
   if ((e = hipMemsetAsync(c->flag, 0, 16, c->st))) return bail(e, "zero flags");
+  // logits columns [Vp, row stride) are never written by the classifier GEMM
+  if ((e = hipMemsetAsync(c->logits, 0, (size_t)c->maxM * c->ldl * c->act_es, c->st)))
+    return bail(e, "zero logits");
   if (c->bf && (e = gk::to_bf16(c->params, c->shadow, c->nflat, c->st))) return bail(e, "bf16 copy");
   // AdamW chunk table
   std::vector<gk::AdamChunk> ch;
