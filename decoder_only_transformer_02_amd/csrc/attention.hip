@@ -52,27 +52,42 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Stage a 64-row x 64-col bf16 tile (rows r0.., column offset col) into LDS
-// as [row][col] (normal) and/or [col][row] (transposed).  Rows >= T are 0.
-template <bool NORMAL, bool TRANS>
-__device__ __forceinline__ void stage_tile(const bf16* base, int ld, int r0, int T, uint16_t* dn,
-                                           uint16_t* dt) {
-  // 512 chunks of 8 elements; 256 threads x 2.  chunk: row = c % 64, oct = c / 64
+// A 64-row x 64-column bf16 tile held in registers between its global load
+// and its LDS store (2 x 16 bytes per thread), so the next tile's loads are
+// in flight while the current one is being consumed.  Rows >= T load as 0.
+struct Tile64 {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const bf16* base, int ld, int r0, int T) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int c = threadIdx.x + i * 256;
-    int row = c & 63, oct = c >> 6;
-    int gr = r0 + row;
-    uint4 v = gr < T ? ldg16(base + (size_t)gr * ld + oct * 8) : make_uint4(0, 0, 0, 0);
-    if (NORMAL) *(uint4*)(dn + row * ALD + oct * 8) = v;
-    if (TRANS) {
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 2; ++i) {
+      int c = threadIdx.x + i * 256;
+      int row = c & 63, oct = c >> 6;
+      int gr = r0 + row;
+      v[i] = gr < T ? ldg16(base + (size_t)gr * ld + oct * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // [row][col] layout
+  __device__ __forceinline__ void store(uint16_t* dn) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int c = threadIdx.x + i * 256;
+      int row = c & 63, oct = c >> 6;
+      *(uint4*)(dn + row * ALD + oct * 8) = v[i];
+    }
+  }
+  // [col][row] layout
+  __device__ __forceinline__ void store_t(uint16_t* dt) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int c = threadIdx.x + i * 256;
+      int row = c & 63, oct = c >> 6;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         dt[(oct * 8 + j) * ALD + row] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
     }
   }
-}
+};
 
 // ------------------------------------------------------------------ forward, hd = 64
 __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv,
@@ -87,6 +102,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
   const int fr = lane & 31, g = lane >> 5;
   const int q = q0 + 32 * w + fr;
   const bf16* base = qkv + (size_t)b * T * ld;
+  const bf16* kbase_p = base + C + h * 64;
+  const bf16* vbase_p = base + 2 * C + h * 64;
 
   bf16x8 qf[4];
 #pragma unroll
@@ -100,12 +117,19 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
   const int ntiles = qlast / 64 + 1;
   const int wq_hi = min(q0 + 32 * w + 31, T - 1);
 
+  Tile64 kt_r, vt_r;
+  kt_r.load(kbase_p, ld, 0, T);
+  vt_r.load(vbase_p, ld, 0, T);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * 64;
     __syncthreads();
-    stage_tile<true, false>(base + C + h * 64, ld, k0, T, Ks, nullptr);
-    stage_tile<false, true>(base + 2 * C + h * 64, ld, k0, T, nullptr, Vt);
+    kt_r.store(Ks);
+    vt_r.store_t(Vt);
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      kt_r.load(kbase_p, ld, k0 + 64, T);
+      vt_r.load(vbase_p, ld, k0 + 64, T);
+    }
     if (k0 > wq_hi) continue;
     f32x16 s[2] = {zero16(), zero16()};
 #pragma unroll
@@ -115,14 +139,17 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
         bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
         s[kb] = mfma(a, qf[ks], s[kb]);
       }
+    const bool diag = k0 + 63 > q0 + 32 * w;  // tile reaches past the wave's first query
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
         float v = s[kb][e] * sl2;
-        if (key > q || key >= T) v = -INFINITY;
+        if (diag) {
+          int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+          if (key > q || key >= T) v = -INFINITY;
+        }
         s[kb][e] = v;
         mx = fmaxf(mx, v);
       }
@@ -172,20 +199,39 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
 }
 
 // ------------------------------------------------------------------ backward preprocessing
-// D[bh, t] = sum_d dO[t, h, d] * O[t, h, d]
+// D[bh, t] = sum_d dO[t, h, d] * O[t, h, d].  One thread per (row, head),
+// 16-byte loads; neighbouring threads read neighbouring heads of one row.
+template <typename TA>
+__device__ __forceinline__ float dot16(const uint4& a, const uint4& b);
+template <>
+__device__ __forceinline__ float dot16<bf16>(const uint4& a, const uint4& b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    s += bfbits2f(x[j] & 0xffffu) * bfbits2f(y[j] & 0xffffu) + bfbits2f(x[j] >> 16) * bfbits2f(y[j] >> 16);
+  return s;
+}
+template <>
+__device__ __forceinline__ float dot16<float>(const uint4& a, const uint4& b) {
+  return __uint_as_float(a.x) * __uint_as_float(b.x) + __uint_as_float(a.y) * __uint_as_float(b.y) +
+         __uint_as_float(a.z) * __uint_as_float(b.z) + __uint_as_float(a.w) * __uint_as_float(b.w);
+}
+
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attn_bwd_pre(const TA* __restrict__ o,
                                                       const TA* __restrict__ dout,
                                                       float* __restrict__ D, int B, int T, int H,
                                                       int hd) {
-  int i = blockIdx.x * 256 + threadIdx.x;  // (b, t, h) flattened as row * H + h
+  constexpr int E = 16 / sizeof(TA);
+  int i = blockIdx.x * 256 + threadIdx.x;  // row * H + h
   if (i >= B * T * H) return;
   int h = i % H, row = i / H;
   int b = row / T, t = row % T;
   const TA* po = o + (size_t)row * H * hd + h * hd;
   const TA* pd = dout + (size_t)row * H * hd + h * hd;
   float s = 0.f;
-  for (int d = 0; d < hd; ++d) s += to_f(po[d]) * to_f(pd[d]);
+  for (int d = 0; d < hd; d += E) s += dot16<TA>(*(const uint4*)(po + d), *(const uint4*)(pd + d));
   D[((size_t)b * H + h) * T + t] = s;
 }
 
@@ -207,6 +253,8 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
   const int q = q0 + 32 * w + fr;
   const bf16* base = qkv + (size_t)b * T * ld;
   const bf16* dob = dout + (size_t)b * T * C;
+  const bf16* kp = base + C + h * 64;
+  const bf16* vp = base + 2 * C + h * 64;
 
   bf16x8 qf[4], dof[4];
 #pragma unroll
@@ -223,40 +271,50 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
   const int ntiles = qlast / 64 + 1;
   const int wq_hi = min(q0 + 32 * w + 31, T - 1);
 
+  Tile64 kr, vr;
+  kr.load(kp, ld, 0, T);
+  vr.load(vp, ld, 0, T);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * 64;
     __syncthreads();
-    stage_tile<true, true>(base + C + h * 64, ld, k0, T, Ks, Kt);
-    stage_tile<true, false>(base + 2 * C + h * 64, ld, k0, T, Vs, nullptr);
+    kr.store(Ks);
+    kr.store_t(Kt);
+    vr.store(Vs);
     __syncthreads();
+    if (kt + 1 < ntiles) {
+      kr.load(kp, ld, k0 + 64, T);
+      vr.load(vp, ld, k0 + 64, T);
+    }
     if (k0 > wq_hi) continue;
-    f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+    const bool diag = k0 + 63 > q0 + 32 * w;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
-        s[kb] = mfma(a, qf[ks], s[kb]);
+        s = mfma(a, qf[ks], s);
         bf16x8 v = __builtin_bit_cast(bf16x8, *(const uint4*)(Vs + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
-        dp[kb] = mfma(v, dof[ks], dp[kb]);
+        dp = mfma(v, dof[ks], dp);
       }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        float p = __builtin_amdgcn_exp2f(s[kb][e] * sl2 - lq);
-        if (key > q || key >= T) p = 0.f;
-        s[kb][e] = p * (dp[kb][e] - Dq);  // dS^T
+        float p = __builtin_amdgcn_exp2f(s[e] * sl2 - lq);
+        if (diag) {
+          int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+          if (key > q || key >= T) p = 0.f;
+        }
+        s[e] = p * (dp[e] - Dq);  // dS^T
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 dsb = pack_slots(s[j >> 1], j & 1);
-      int kbase = (j >> 1) * 32 + (j & 1) * 16 + g * 4;
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 dsb = pack_slots(s, hh);
+        int kbase = kb * 32 + hh * 16 + g * 4;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        bf16x8 a = lds_two_runs(Kt + (db * 32 + fr) * ALD, kbase);
-        dq[db] = mfma(a, dsb, dq[db]);
+        for (int db = 0; db < 2; ++db) {
+          bf16x8 a = lds_two_runs(Kt + (db * 32 + fr) * ALD, kbase);
+          dq[db] = mfma(a, dsb, dq[db]);
+        }
       }
     }
   }
@@ -274,7 +332,7 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
 }
 
 // ------------------------------------------------------------------ dK, dV, hd = 64
-__global__ __launch_bounds__(256) void k_attn_dkv64(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dkv64(const bf16* __restrict__ qkv,
                                                     const bf16* __restrict__ dout,
                                                     const float* __restrict__ lse,
                                                     const float* __restrict__ Dv,
@@ -293,6 +351,8 @@ __global__ __launch_bounds__(256) void k_attn_dkv64(const bf16* __restrict__ qkv
   const int key = k0 + 32 * w + fr;
   const bf16* base = qkv + (size_t)b * T * ld;
   const bf16* dob = dout + (size_t)b * T * C;
+  const bf16* qp = base + h * 64;
+  const bf16* op = dob + h * 64;
 
   bf16x8 kf[4], vf[4];
 #pragma unroll
@@ -305,52 +365,76 @@ __global__ __launch_bounds__(256) void k_attn_dkv64(const bf16* __restrict__ qkv
   f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
   const int wk_lo = k0 + 32 * w;
   const int nqt = (T + 63) / 64;
-  for (int qt = k0 / 64; qt < nqt; ++qt) {
+  const int qt0 = k0 / 64;
+  Tile64 qr, orr;
+  float lr = 0.f, dr = 0.f;
+  auto load_q = [&](int qt) {
+    qr.load(qp, ld, qt * 64, T);
+    orr.load(op, C, qt * 64, T);
+    if (tid < 64) {
+      int qq = qt * 64 + tid;
+      lr = qq < T ? lse[(size_t)bh * T + qq] : 0.f;
+      dr = qq < T ? Dv[(size_t)bh * T + qq] : 0.f;
+    }
+  };
+  load_q(qt0);
+  for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * 64;
     __syncthreads();
-    stage_tile<true, true>(base + h * 64, ld, q0, T, Qs, Qt);
-    stage_tile<true, true>(dob + h * 64, C, q0, T, Os, Ot);
+    qr.store(Qs);
+    qr.store_t(Qt);
+    orr.store(Os);
+    orr.store_t(Ot);
     if (tid < 64) {
-      int qq = q0 + tid;
-      Ls[tid] = qq < T ? lse[(size_t)bh * T + qq] : 0.f;
-      Ds[tid] = qq < T ? Dv[(size_t)bh * T + qq] : 0.f;
+      Ls[tid] = lr;
+      Ds[tid] = dr;
     }
     __syncthreads();
+    if (qt + 1 < nqt) load_q(qt + 1);
     if (q0 + 63 < wk_lo || wk_lo >= T) continue;
-    // S [q x key] and dP [q x key]: rows q = q0 + qb*32 + 8(e/4) + 4g + e%4
-    f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+    const bool diag = q0 < wk_lo + 31;  // some (q, key) pairs of the tile are masked
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+      // S and dP for 32 queries x this wave's 32 keys:
+      // rows q = q0 + qb*32 + 8(e/4) + 4g + e%4, column key
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Qs + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
-        s[qb] = mfma(a, kf[ks], s[qb]);
+        s = mfma(a, kf[ks], s);
         bf16x8 o = __builtin_bit_cast(bf16x8, *(const uint4*)(Os + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
-        dp[qb] = mfma(o, vf[ks], dp[qb]);
-      }
-    f32x16 ds[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int ql = qb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        int qq = q0 + ql;
-        float p = __builtin_amdgcn_exp2f(s[qb][e] * sl2 - Ls[ql]);
-        if (key > qq || qq >= T) p = 0.f;
-        s[qb][e] = p;
-        ds[qb][e] = p * (dp[qb][e] - Ds[ql]);
+        dp = mfma(o, vf[ks], dp);
       }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 pb = pack_slots(s[j >> 1], j & 1);
-      bf16x8 dsb = pack_slots(ds[j >> 1], j & 1);
-      int qbase = (j >> 1) * 32 + (j & 1) * 16 + g * 4;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int ql0 = qb * 32 + e4 * 8 + g * 4;
+        const float4 L4 = *(const float4*)(Ls + ql0);
+        const float4 D4 = *(const float4*)(Ds + ql0);
+        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        bf16x8 ao = lds_two_runs(Ot + (db * 32 + fr) * ALD, qbase);
-        dv[db] = mfma(ao, pb, dv[db]);
-        bf16x8 aq = lds_two_runs(Qt + (db * 32 + fr) * ALD, qbase);
-        dk[db] = mfma(aq, dsb, dk[db]);
+        for (int e1 = 0; e1 < 4; ++e1) {
+          const int e = e4 * 4 + e1;
+          float p = __builtin_amdgcn_exp2f(s[e] * sl2 - Lr[e1]);
+          if (diag) {
+            int qq = q0 + ql0 + e1;
+            if (key > qq || qq >= T) p = 0.f;
+          }
+          s[e] = p;
+          dp[e] = p * (dp[e] - Dr[e1]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pb = pack_slots(s, hh);
+        bf16x8 dsb = pack_slots(dp, hh);
+        int qbase = qb * 32 + hh * 16 + g * 4;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          bf16x8 ao = lds_two_runs(Ot + (db * 32 + fr) * ALD, qbase);
+          dv[db] = mfma(ao, pb, dv[db]);
+          bf16x8 aq = lds_two_runs(Qt + (db * 32 + fr) * ALD, qbase);
+          dk[db] = mfma(aq, dsb, dk[db]);
+        }
       }
     }
   }
@@ -491,7 +575,7 @@ hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, i
 
 hipError_t attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, void* dqkv,
                     float* ws, int B, int T, int H, int hd, bool bf, hipStream_t st) {
-  if (hd > 128) return hipErrorInvalidValue;
+  if (hd > 128 || hd % 8) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)hd);
   const float sl2 = scale * LOG2E_F;
   int n = B * T * H;

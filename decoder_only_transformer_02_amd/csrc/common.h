@@ -12,13 +12,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define WAVE 64
 
-// Round-to-nearest-even float -> bf16 (NaN kept a quiet NaN).
-__device__ __forceinline__ uint16_t f2bf_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bf16 (the gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float bfbits2f(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Element conversion for the two storage types of activations.
@@ -31,16 +28,17 @@ template <> struct Cvt<bf16> {
   static __device__ __forceinline__ float to_f(bf16 x) {
     return bfbits2f(__builtin_bit_cast(uint16_t, x));
   }
-  static __device__ __forceinline__ bf16 from_f(float x) {
-    return __builtin_bit_cast(bf16, f2bf_bits(x));
-  }
+  static __device__ __forceinline__ bf16 from_f(float x) { return (__bf16)x; }
 };
 template <typename T> __device__ __forceinline__ float to_f(T x) { return Cvt<T>::to_f(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return Cvt<T>::from_f(x); }
 
 // Two floats -> packed pair of bf16 in one dword (low = a).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf_bits(a) | ((uint32_t)f2bf_bits(b) << 16);
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Wavefront (64 lanes) all-reduce.

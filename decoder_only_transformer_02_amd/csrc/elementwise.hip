@@ -229,54 +229,109 @@ hipError_t ln_bwd(const float* x, const float* mean, const float* rstd, const fl
   return hipGetLastError();
 }
 
-// dw[c] = beta * dw[c] + sum_b part[b][0][c]; db likewise (float64 sum, fixed order).
-__global__ __launch_bounds__(256) void k_ln_param_reduce(const float* __restrict__ part, int nblk,
-                                                         float* dw, float* db, int C, float beta) {
+// dw[c] = beta * dw[c] + sum_b part[b][0][c]; db likewise.  Stage 1: blocks
+// of 64 columns x 4 row groups sum a slice of the partial rows; stage 2 sums
+// the slices (fixed order, so deterministic).
+constexpr int LNR_SLICES = 16;
+
+__global__ __launch_bounds__(256) void k_ln_param_reduce1(const float* __restrict__ part, int nblk,
+                                                          int C, float* __restrict__ part2) {
+  __shared__ float red[4][64];
+  int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  int wb = blockIdx.y;                  // 0: dw, 1: db
+  int grp = threadIdx.x >> 6;
+  int per = (nblk + LNR_SLICES - 1) / LNR_SLICES;
+  int r0 = blockIdx.z * per, r1 = min(r0 + per, nblk);
+  float s = 0.f;
+  if (c < C)
+    for (int r = r0 + grp; r < r1; r += 4) s += part[((size_t)r * 2 + wb) * C + c];
+  red[grp][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (grp == 0 && c < C) {
+    int l = threadIdx.x & 63;
+    part2[((size_t)blockIdx.z * 2 + wb) * C + c] = (red[0][l] + red[1][l]) + (red[2][l] + red[3][l]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ln_param_reduce2(const float* __restrict__ part2, int C,
+                                                          float* dw, float* db, float beta) {
   int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
-  double a = 0.0, b = 0.0;
-  for (int i = 0; i < nblk; ++i) {
-    a += part[((size_t)i * 2 + 0) * C + c];
-    b += part[((size_t)i * 2 + 1) * C + c];
-  }
-  dw[c] = (beta != 0.f ? beta * dw[c] : 0.f) + (float)a;
-  db[c] = (beta != 0.f ? beta * db[c] : 0.f) + (float)b;
+  float* out = blockIdx.y == 0 ? dw : db;
+  float s = 0.f;
+  for (int z = 0; z < LNR_SLICES; ++z) s += part2[((size_t)z * 2 + blockIdx.y) * C + c];
+  out[c] = (beta != 0.f ? beta * out[c] : 0.f) + s;
 }
 
 hipError_t ln_param_grad_reduce(const float* part, int nblk, float* dw, float* db, int C,
                                 float beta, hipStream_t st) {
-  k_ln_param_reduce<<<cdiv(C, 256), 256, 0, st>>>(part, nblk, dw, db, C, beta);
+  // part2 lives right after the nblk partial rows in the same workspace
+  float* part2 = const_cast<float*>(part) + (size_t)nblk * 2 * C;
+  k_ln_param_reduce1<<<dim3(cdiv(C, 64), 2, LNR_SLICES), 256, 0, st>>>(part, nblk, C, part2);
+  k_ln_param_reduce2<<<dim3(cdiv(C, 256), 2), 256, 0, st>>>(part2, C, dw, db, beta);
   return hipGetLastError();
 }
 
+int ln_bwd_part_floats(int M, int C) { return (ln_bwd_blocks(M) + LNR_SLICES) * 2 * C; }
+
 // ------------------------------------------------------------------ bias-gradient column sums
 int colsum_parts(int M) {
-  int r = cdiv(M, 64);
-  return r < 128 ? r : 128;
+  int r = cdiv(M, 256);
+  return r < 64 ? r : 64;
 }
 
+// Stage 1: a block covers 256 columns (32 threads x 8 columns, 16-byte
+// loads) and 8 row groups over one slice of rows; stage 2 sums the slices.
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum_part(const T* __restrict__ X, int M, int N, int ldx,
                                                      int rows_per, float* __restrict__ part) {
-  int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  int r0 = blockIdx.y * rows_per, r1 = min(r0 + rows_per, M);
-  float s = 0.f;
-  for (int m = r0; m < r1; ++m) s += to_f(X[(size_t)m * ldx + n]);
-  part[(size_t)blockIdx.y * N + n] = s;
+  constexpr int E = 16 / sizeof(T);           // columns per 16-byte load
+  constexpr int TPR = 256 / 8;                // threads across one row segment
+  __shared__ float red[8][TPR * 8];
+  const int tc = threadIdx.x % TPR, g = threadIdx.x / TPR;
+  const int n0 = blockIdx.x * (TPR * 8);
+  const int r0 = blockIdx.y * rows_per, r1 = min(r0 + rows_per, M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c8 = 0; c8 < 8; c8 += E) {
+    int n = n0 + tc * 8 + c8;
+    if (n >= N) break;
+    for (int m = r0 + g; m < r1; m += 8) {
+      uint4 u = *(const uint4*)(X + (size_t)m * ldx + n);
+      if constexpr (E == 8) {
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[c8 + j] += bfbits2f((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+      } else {
+        acc[c8 + 0] += __uint_as_float(u.x); acc[c8 + 1] += __uint_as_float(u.y);
+        acc[c8 + 2] += __uint_as_float(u.z); acc[c8 + 3] += __uint_as_float(u.w);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[g][tc * 8 + j] = acc[j];
+  __syncthreads();
+  int col = threadIdx.x;  // 256 columns of this block
+  int n = n0 + col;
+  if (n < N) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += red[k][col];
+    part[(size_t)blockIdx.y * N + n] = s;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ part, int R, int N,
                                                       float* db, float beta) {
   int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
-  double s = 0.0;
+  float s = 0.f;
   for (int r = 0; r < R; ++r) s += part[(size_t)r * N + n];
-  db[n] = (beta != 0.f ? beta * db[n] : 0.f) + (float)s;
+  db[n] = (beta != 0.f ? beta * db[n] : 0.f) + s;
 }
 
 hipError_t colsum(const void* X, bool x_bf16, int M, int N, int ldx, float* db, float beta,
                   float* part, hipStream_t st) {
+  if (N % 8 || ldx % 8) return hipErrorInvalidValue;
   int R = colsum_parts(M);
   int rows_per = cdiv(M, R);
   dim3 g(cdiv(N, 256), R);

@@ -92,7 +92,8 @@ bool config_ok(const gpt2_config* c, std::string* why) {
   if (c->n_layer < 1 || c->n_head < 1 || c->n_embd < 64) return bad("bad layer/head/embd");
   if (c->n_embd % 64 || c->n_embd > 1024) return bad("n_embd must be a multiple of 64, <= 1024");
   if (c->n_embd % c->n_head) return bad("n_embd % n_head != 0");
-  if ((c->n_embd / c->n_head) > 128) return bad("head_dim > 128");
+  if ((c->n_embd / c->n_head) > 128 || (c->n_embd / c->n_head) % 8)
+    return bad("head_dim must be a multiple of 8, <= 128");
   if (c->vocab_size < 2 || c->padded_vocab < c->vocab_size) return bad("bad vocab sizes");
   if (c->padded_vocab > 65536) return bad("padded_vocab > 65536");
   if (c->block_size < 1 || c->max_seq < 1 || c->max_seq > c->block_size) return bad("bad seq sizes");
@@ -258,7 +259,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t o_dattn = pl.add("d_attn", GPT2_K_ACT, adt, {maxM, C});
   size_t o_dqkv = pl.add("d_qkv", GPT2_K_ACT, adt, {maxM, 3 * C});
   size_t o_du = pl.add("d_fc_u", GPT2_K_ACT, adt, {maxM, 4 * C});
-  size_t o_lnp = pl.raw((size_t)gk::ln_bwd_blocks((int)maxM) * 2 * C * 4);
+  size_t o_lnp = pl.raw((size_t)gk::ln_bwd_part_floats((int)maxM, C) * 4);
   size_t o_colp = pl.raw((size_t)gk::colsum_parts((int)maxM) * 4 * C * 4);
   size_t sk = 0;
   {

@@ -64,6 +64,58 @@ __device__ __forceinline__ void epi_store(const GP& p, int r, int c, float acc) 
   }
 }
 
+// Four consecutive output columns c..c+3 of row r (bf16 activations).
+template <int EPI>
+__device__ __forceinline__ void epi_store4(const GP& p, int r, int c, float v0, float v1, float v2,
+                                           float v3) {
+  if (r >= p.M) return;
+  if (c + 3 >= p.N) {
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c + j < p.N) epi_store<EPI, bf16>(p, r, c + j, v[j]);
+    return;
+  }
+  const size_t o = (size_t)r * p.ldo + c;
+  if constexpr (EPI == EPI_STORE) {
+    float4 b = p.bias ? *(const float4*)(p.bias + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(p.alpha * v0 + b.x, p.alpha * v1 + b.y),
+                                             pack_bf2(p.alpha * v2 + b.z, p.alpha * v3 + b.w));
+  } else if constexpr (EPI == EPI_LOGITS) {
+    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+  } else if constexpr (EPI == EPI_GELU) {
+    float4 b = *(const float4*)(p.bias + c);
+    float u0 = v0 + b.x, u1 = v1 + b.y, u2 = v2 + b.z, u3 = v3 + b.w;
+    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(u0, u1), pack_bf2(u2, u3));
+    *(uint2*)((bf16*)p.out2 + o) = make_uint2(pack_bf2(gelu_tanh_f(u0), gelu_tanh_f(u1)),
+                                              pack_bf2(gelu_tanh_f(u2), gelu_tanh_f(u3)));
+  } else if constexpr (EPI == EPI_RESID) {
+    float4 b = *(const float4*)(p.bias + c);
+    float4 x = *(const float4*)((const float*)p.aux + o);
+    *(float4*)((float*)p.out + o) = make_float4(x.x + v0 + b.x, x.y + v1 + b.y, x.z + v2 + b.z,
+                                                x.w + v3 + b.w);
+  } else if constexpr (EPI == EPI_DGELU) {
+    uint2 uu = *(const uint2*)((const bf16*)p.aux + o);
+    float u0 = bfbits2f(uu.x & 0xffffu), u1 = bfbits2f(uu.x >> 16);
+    float u2 = bfbits2f(uu.y & 0xffffu), u3 = bfbits2f(uu.y >> 16);
+    *(uint2*)((bf16*)p.out + o) =
+        make_uint2(pack_bf2(v0 * gelu_tanh_grad_f(u0), v1 * gelu_tanh_grad_f(u1)),
+                   pack_bf2(v2 * gelu_tanh_grad_f(u2), v3 * gelu_tanh_grad_f(u3)));
+  } else {  // EPI_WGRAD
+    float* op = (float*)p.out + (size_t)blockIdx.z * ((size_t)p.M * p.ldo);
+    if (gridDim.z > 1) {
+      *(float4*)(op + o) = make_float4(v0, v1, v2, v3);
+    } else {
+      float4 w = make_float4(p.alpha * v0, p.alpha * v1, p.alpha * v2, p.alpha * v3);
+      if (p.beta != 0.f) {
+        float4 old = *(const float4*)(op + o);
+        w.x += p.beta * old.x; w.y += p.beta * old.y; w.z += p.beta * old.z; w.w += p.beta * old.w;
+      }
+      *(float4*)(op + o) = w;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA kernel
 constexpr int BK = 64;       // K tile (bf16 elements)
 constexpr int LDS_LD = 72;   // padded LDS row (elements): 144 B, 16-byte aligned
@@ -94,12 +146,17 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[KR], uint32_t 
 // registers, written as 8 rows of KR k-values.
 template <int ROWS, int NT, bool TRANS>
 struct TileLoader {
-  static constexpr int KR = ((BK / 8) * (ROWS / 8) >= NT) ? 8 : 4;
+  // KR = 8 unless only KR = 4 splits the blocks evenly over the threads;
+  // an uneven split leaves the last round to the first threads.
+  static constexpr int KR = (((BK / 8) * (ROWS / 8)) % NT == 0) ? 8
+                            : (((BK / 4) * (ROWS / 8)) % NT == 0) ? 4 : 8;
   static constexpr int KG = BK / KR;                       // k groups per tile
-  static constexpr int NBLK = TRANS ? (KG * (ROWS / 8)) / NT : 0;
+  static constexpr int TOT = KG * (ROWS / 8);              // transposed blocks per tile
+  static constexpr int NBLK = TRANS ? (TOT + NT - 1) / NT : 0;
+  static constexpr bool EVEN = TOT % NT == 0;
   static constexpr int NCH = TRANS ? NBLK * KR : (ROWS * BK / 8) / NT;
   static_assert(NCH >= 1, "tile too small for the thread count");
-  static_assert(!TRANS || NBLK * NT == KG * (ROWS / 8), "transposed tile must split evenly");
+  static_assert(TRANS || (ROWS * BK / 8) % NT == 0, "K-contiguous tile must split evenly");
   uint4 r[NCH];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long ld, int row0,
@@ -121,10 +178,11 @@ struct TileLoader {
         int b = tid + bi * NT;
         int ko = b % KG, ro = b / KG;
         int grow = row0 + ro * 8;
+        const bool live = EVEN || b < TOT;
 #pragma unroll
         for (int i = 0; i < KR; ++i) {
           int gk = k0 + ko * KR + i;
-          if (gk < K && grow < nrows)
+          if (live && gk < K && grow < nrows)
             r[bi * KR + i] = ld16(base + (size_t)gk * ld + grow);
           else
             r[bi * KR + i] = make_uint4(0, 0, 0, 0);
@@ -145,6 +203,7 @@ struct TileLoader {
 #pragma unroll
       for (int bi = 0; bi < NBLK; ++bi) {
         int b = tid + bi * NT;
+        if (!EVEN && b >= TOT) continue;
         int ko = b % KG, ro = b / KG;
         uint4 in[KR];
         uint32_t out[8][KR / 2];
@@ -219,49 +278,55 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
   }
   __syncthreads();
 
-  const int fr = lane & 31;        // fragment row / column
+  const int fr = lane & 31;        // fragment row (m for A, n for B)
   const int fk = (lane >> 5) * 8;  // k offset inside a 16-wide k step
+  // D = B_frag x A_frag: the accumulator is the transposed 32x32 block, so a
+  // lane holds one output row and 4 runs of 4 consecutive output columns.
+  auto substep = [&](const uint16_t* As, const uint16_t* Bs, int ks) {
+    bf16x8 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (wm + i * 32 + fr) * LDS_LD + ks * 16 + fk));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8, *(const uint4*)(Bs + (wn + j * 32 + fr) * LDS_LD + ks * 16 + fk));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {
+    const bool nxt = kt + 1 < nk;
+    if (nxt) {
       la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend, tid);
       lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend, tid);
     }
     const uint16_t* As = &lds[cur][0];
     const uint16_t* Bs = &lds[cur][BM * LDS_LD];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (wm + i * 32 + fr) * LDS_LD + ks * 16 + fk));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *(const uint4*)(Bs + (wn + j * 32 + fr) * LDS_LD + ks * 16 + fk));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
+    substep(As, Bs, 0);
+    substep(As, Bs, 1);
+    if (nxt) {
       la.store(&lds[cur ^ 1][0], tid);
       lb.store(&lds[cur ^ 1][BM * LDS_LD], tid);
     }
+    substep(As, Bs, 2);
+    substep(As, Bs, 3);
     __syncthreads();
   }
 
-  // accumulator layout of a 32x32 block: lane l holds column l % 32 and
-  // rows 8 * (e / 4) + 4 * (l / 32) + e % 4
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int r = m0 + wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        int c = n0 + wn + j * 32 + fr;
-        epi_store<EPI, bf16>(p, r, c, acc[i][j][e]);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        int r = m0 + wm + i * 32 + fr;
+        int c = n0 + wn + j * 32 + e4 * 8 + (lane >> 5) * 4;
+        epi_store4<EPI>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                        acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
       }
 }
 
@@ -316,46 +381,88 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GP p) {
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int S,
                                                        size_t n, float* out, float alpha,
                                                        float beta) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    float s = 0.f;
-    for (int z = 0; z < S; ++z) s += ws[(size_t)z * n + i];
-    float v = alpha * s;
-    if (beta != 0.f) v += beta * out[i];
-    out[i] = v;
+  const size_t n4 = n / 4;  // n is a multiple of 4 (N % 4 == 0 when split)
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < S; ++z) {
+      float4 v = *(const float4*)(ws + (size_t)z * n + 4 * i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    float4 r = make_float4(alpha * s.x, alpha * s.y, alpha * s.z, alpha * s.w);
+    if (beta != 0.f) {
+      float4 o = *(const float4*)(out + 4 * i);
+      r.x += beta * o.x; r.y += beta * o.y; r.z += beta * o.z; r.w += beta * o.w;
+    }
+    *(float4*)(out + 4 * i) = r;
   }
 }
 
 // ------------------------------------------------------------------ dispatch
-static int splitk_for(int M, int N, int K, int bm, int bn) {
-  long tiles = (long)cdiv(M, bm) * cdiv(N, bn);
-  int s = 1;
-  while (tiles * s < 512 && K / (s * 2) >= 1024 && s < 16) s *= 2;
-  return s;
+// Tile shapes (block BM x BN, 2 x 2 waves) and a simple cost model: MFMA
+// time of the waves of workgroups the grid needs on 256 CUs (relative
+// efficiency per shape), plus the HBM time of the split-K partials.
+struct TileCfg {
+  int bm, bn, per_cu;
+  double eff;
+};
+static const TileCfg kCfgs[4] = {{256, 256, 1, 1.00}, {256, 192, 1, 0.96}, {256, 128, 1, 0.88},
+                                 {128, 128, 2, 0.60}};
+
+struct Plan {
+  int cfg, splits, kchunk;
+};
+
+static Plan plan_gemm(int M, int N, int K, bool wgrad, size_t ws_elems) {
+  const double cu_flops = 2.5e15 / 256.0, hbm = 6.0e12;
+  Plan best{3, 1, cdiv(K, BK) * BK};
+  double best_t = 1e30;
+  for (int ci = 0; ci < 4; ++ci) {
+    const TileCfg& t = kCfgs[ci];
+    long tiles = (long)cdiv(M, t.bm) * cdiv(N, t.bn);
+    for (int S = 1; S <= (wgrad ? 32 : 1); ++S) {
+      int kchunk = cdiv(cdiv(K, S), BK) * BK;
+      if (cdiv(K, kchunk) != S) continue;
+      if (S > 1 && (size_t)S * M * N > ws_elems) continue;
+      long wg = tiles * S;
+      long waves = (wg + 256L * t.per_cu - 1) / (256L * t.per_cu);
+      double tm = waves * t.per_cu * (2.0 * t.bm * t.bn * kchunk) / (cu_flops * t.eff);
+      double tr = S > 1 ? ((double)S + 2.0) * M * N * 4.0 / hbm + 3e-6 : 0.0;
+      if (tm + tr < best_t) {
+        best_t = tm + tr;
+        best = Plan{ci, S, kchunk};
+      }
+    }
+  }
+  return best;
 }
 
 size_t gemm_splitk_ws_elems(int M, int N, int K) {
-  int s = splitk_for(M, N, K, 128, 128);
-  return s > 1 ? (size_t)s * M * N : 0;
+  Plan pl = plan_gemm(M, N, K, true, (size_t)-1);
+  return pl.splits > 1 ? (size_t)pl.splits * M * N : 0;
+}
+
+template <int BM, int BN, bool AT, bool BT, int EPI>
+static void launch_cfg(GP q, int S, hipStream_t st) {
+  int nb = cdiv(q.M, BM) * cdiv(q.N, BN);
+  k_gemm_bf16<BM, BN, 2, 2, AT, BT, EPI><<<dim3(nb, 1, S), 256, 0, st>>>(q);
 }
 
 template <bool AT, bool BT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
-  int nm = cdiv(a.M, BM), nn = cdiv(a.N, BN);
-  int S = 1;
-  if constexpr (EPI == EPI_WGRAD) {
-    S = splitk_for(a.M, a.N, a.K, BM, BN);
-    if (a.ldo != a.N || !a.splitk_ws || (size_t)S * a.M * a.N > a.splitk_ws_elems) S = 1;
-  }
-  int kchunk = cdiv(cdiv(a.K, S), BK) * BK;
-  S = cdiv(a.K, kchunk);
-  p.kchunk = kchunk;
+  const bool wg = EPI == EPI_WGRAD && a.ldo == a.N && a.splitk_ws;
+  Plan pl = plan_gemm(a.M, a.N, a.K, wg, wg ? a.splitk_ws_elems : 0);
+  p.kchunk = pl.kchunk;
   GP q = p;
-  if (S > 1) q.out = a.splitk_ws;
-  k_gemm_bf16<BM, BN, WM, WN, AT, BT, EPI><<<dim3(nm * nn, 1, S), WM * WN * 64, 0, st>>>(q);
-  if (S > 1) {
+  if (pl.splits > 1) q.out = a.splitk_ws;
+  switch (pl.cfg) {
+    case 0: launch_cfg<256, 256, AT, BT, EPI>(q, pl.splits, st); break;
+    case 1: launch_cfg<256, 192, AT, BT, EPI>(q, pl.splits, st); break;
+    case 2: launch_cfg<256, 128, AT, BT, EPI>(q, pl.splits, st); break;
+    default: launch_cfg<128, 128, AT, BT, EPI>(q, pl.splits, st); break;
+  }
+  if (pl.splits > 1) {
     size_t n = (size_t)a.M * a.N;
-    k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, S, n, (float*)a.out, a.alpha, a.beta);
+    k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, pl.splits, n, (float*)a.out, a.alpha, a.beta);
   }
   return hipGetLastError();
 }
@@ -367,18 +474,30 @@ static hipError_t launch_f32(const GemmArgs& a, GP p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Operand layouts used by the step: forward NT (A, B K-contiguous) with the
+// store / classifier / GELU / residual epilogues; dX as NN (B transposed)
+// with the store / GELU-derivative epilogues; dW as TN (both transposed).
 template <int EPI>
 static hipError_t dispatch_t(const GemmArgs& a, const GP& p, hipStream_t st) {
+  constexpr bool NT_OK = EPI == EPI_STORE || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr bool NN_OK = EPI == EPI_STORE || EPI == EPI_DGELU;
+  constexpr bool TN_OK = EPI == EPI_WGRAD;
   if (a.bf16) {
-    if (!a.a_t && !a.b_t) return launch_bf16<false, false, EPI>(a, p, st);
-    if (!a.a_t && a.b_t) return launch_bf16<false, true, EPI>(a, p, st);
-    if (a.a_t && a.b_t) return launch_bf16<true, true, EPI>(a, p, st);
-    return launch_bf16<true, false, EPI>(a, p, st);
+    if constexpr (NT_OK)
+      if (!a.a_t && !a.b_t) return launch_bf16<false, false, EPI>(a, p, st);
+    if constexpr (NN_OK)
+      if (!a.a_t && a.b_t) return launch_bf16<false, true, EPI>(a, p, st);
+    if constexpr (TN_OK)
+      if (a.a_t && a.b_t) return launch_bf16<true, true, EPI>(a, p, st);
+    return hipErrorInvalidValue;
   }
-  if (!a.a_t && !a.b_t) return launch_f32<false, false, EPI>(a, p, st);
-  if (!a.a_t && a.b_t) return launch_f32<false, true, EPI>(a, p, st);
-  if (a.a_t && a.b_t) return launch_f32<true, true, EPI>(a, p, st);
-  return launch_f32<true, false, EPI>(a, p, st);
+  if constexpr (NT_OK)
+    if (!a.a_t && !a.b_t) return launch_f32<false, false, EPI>(a, p, st);
+  if constexpr (NN_OK)
+    if (!a.a_t && a.b_t) return launch_f32<false, true, EPI>(a, p, st);
+  if constexpr (TN_OK)
+    if (a.a_t && a.b_t) return launch_f32<true, true, EPI>(a, p, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemm(const GemmArgs& a, hipStream_t st) {

@@ -19,6 +19,7 @@ hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, bool 
 // dres in the activation type; per-block dw/db partials into part
 // ([nblk, 2, C]); then ln_param_grad_reduce folds them into dw/db.
 int ln_bwd_blocks(int M);
+int ln_bwd_part_floats(int M, int C);  // workspace floats for part (+ reduction slices)
 hipError_t ln_bwd(const float* x, const float* mean, const float* rstd, const float* w,
                   const void* dy, bool act_bf16, float* dres, void* dres_act, bool accum,
                   float* part, int M, int C, hipStream_t st);
