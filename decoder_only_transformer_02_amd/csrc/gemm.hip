@@ -306,14 +306,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
     }
     const uint16_t* As = &lds[cur][0];
     const uint16_t* Bs = &lds[cur][BM * LDS_LD];
-    substep(As, Bs, 0);
-    substep(As, Bs, 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) substep(As, Bs, ks);
+    // the next tile's loads had the whole k step to arrive
     if (nxt) {
       la.store(&lds[cur ^ 1][0], tid);
       lb.store(&lds[cur ^ 1][BM * LDS_LD], tid);
     }
-    substep(As, Bs, 2);
-    substep(As, Bs, 3);
     __syncthreads();
   }
 
@@ -328,6 +327,235 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
         epi_store4<EPI>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
                         acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
       }
+}
+
+// ------------------------------------------------------------------ bf16 NT kernel, direct-to-LDS
+// Both operands K-contiguous.  Persistent workgroups walk an XCD-grouped
+// tile order; the K loop runs in stages of 32 k held in an NS-deep LDS ring
+// that global_load_lds_dwordx4 fills directly (no VGPR staging), NS - 1
+// stages ahead, continuing across tile boundaries so the next tile's loads
+// are in flight during the epilogue.  LDS rows are 64 bytes (4 chunks of 8
+// k); chunk c of row r sits in slot c ^ ((r >> 2) & 3), which keeps both the
+// lane-linear direct loads and the 32-row MFMA fragment reads conflict free.
+constexpr int NK = 32;  // k per stage
+constexpr int NS = 4;   // LDS ring depth
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would also wait for every in-flight LDS DMA load (vmcnt 0) and collapse the
+// ring to depth one.  Callers wait for the stage they need (vmcnt) first;
+// LDS stores of this wave are drained here.
+__device__ __forceinline__ void stage_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // compiler-only: keep LDS accesses on their side
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from base + voff + soff (range-checked against nbytes,
+// zero outside) into LDS at lds + 16 * lane.
+__device__ __attribute__((always_inline)) inline void buffer_load_lds16(void* base, uint32_t nbytes,
+                                                                       uint16_t* lds, uint32_t voff,
+                                                                       uint32_t soff) {
+  auto rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// One operand's stage loads: NI buffer loads of 16 bytes per lane per stage,
+// each filling one 16-row block of the LDS tile.  The per-lane byte offsets
+// are loop invariant; the tile row and k position move in the scalar offset.
+// Rows past the end of the operand read as zero (buffer range check).
+template <int ROWS, int NW>
+struct BufLoader {
+  static constexpr int NI = ROWS * 4 / 64 / NW;  // 16-row blocks per wave per stage
+  static_assert(NI * 64 * NW == ROWS * 4, "rows must split over the waves");
+  void* base;
+  uint32_t nbytes;
+  uint32_t voff[NI];
+  int blk0;
+  __device__ __forceinline__ void init(const void* b, long ld, int nrows, int wv, int lane) {
+    uint64_t bytes = (uint64_t)nrows * ld * 2;
+    base = const_cast<void*>(b);
+    nbytes = (uint32_t)(bytes > 0xffffffffull ? 0xffffffffull : bytes);
+    blk0 = wv * NI;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (blk0 + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      voff[i] = (uint32_t)((long)r * ld * 2 + c * 16);
+    }
+  }
+  // soff: byte offset of (row0, k0)
+  __device__ __forceinline__ void issue(uint32_t soff, uint16_t* lds_op) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) buffer_load_lds16(base, nbytes, lds_op + (blk0 + i) * 512, voff[i], soff);
+  }
+};
+
+// Ragged last stage (k0 + 32 > K): zero-filled register loads, LDS stores.
+template <int ROWS, int NW>
+__device__ __forceinline__ void issue_tail(const uint16_t* __restrict__ g, long ld, int row0,
+                                           int nrows, int k0, int K, uint16_t* lds_op, int wv,
+                                           int lane) {
+  constexpr int NI = ROWS * 4 / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = wv * NI + i;
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int gr = row0 + r, gk = k0 + c * 8;
+    uint4 v = (gr < nrows && gk < K) ? *(const uint4*)(g + (size_t)gr * ld + gk)
+                                      : make_uint4(0, 0, 0, 0);
+    *(uint4*)(lds_op + blk * 512 + lane * 8) = v;
+  }
+}
+
+__device__ __forceinline__ int tile_pid(int round, int G) {
+  const int b = blockIdx.x;
+  return round * G + (b & 7) * (G >> 3) + (b >> 3);
+}
+
+__device__ __forceinline__ void grouped_coords(int pid, int nm, int nn, int& tm, int& tn) {
+  constexpr int GROUP_M = 8;
+  int group = GROUP_M * nn;
+  int gid = pid / group;
+  int first = gid * GROUP_M;
+  int gsz = min(nm - first, GROUP_M);
+  int in = pid % group;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int STAGE = (BM + BN) * NK;  // bf16 elements per stage
+  constexpr int PER = BufLoader<BM, NW>::NI + BufLoader<BN, NW>::NI;  // loads per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = (wv / WN) * TM, wn = (wv % WN) * TN;
+  const int fr = lane & 31, g = lane >> 5;
+  const int swz = (fr >> 2) & 3;
+  const int nm = cdiv(p.M, BM), nn = cdiv(p.N, BN);
+  const int tiles = nm * nn;
+  const int G = gridDim.x;
+  const int nk = cdiv(p.K, NK);
+  int my_n = 0;
+  while (tile_pid(my_n, G) < tiles) ++my_n;
+  const int total = my_n * nk;
+  const bool ragged = (p.K % NK) != 0;
+
+  BufLoader<BM, NW> la;
+  BufLoader<BN, NW> lb;
+  la.init(p.A, p.lda, p.M, wv, lane);
+  lb.init(p.B, p.ldb, p.N, wv, lane);
+
+  // issue-side cursor: stage t = (round, kt)
+  int i_round = 0, i_kt = 0, i_tm = 0, i_tn = 0;
+  if (total > 0) grouped_coords(tile_pid(0, G), nm, nn, i_tm, i_tn);
+  auto issue_next = [&](int t) {
+    uint16_t* st = lds + (t % NS) * STAGE;
+    const int k0 = i_kt * NK;
+    if (ragged && k0 + NK > p.K) {
+      issue_tail<BM, NW>((const uint16_t*)p.A, p.lda, i_tm * BM, p.M, k0, p.K, st, wv, lane);
+      issue_tail<BN, NW>((const uint16_t*)p.B, p.ldb, i_tn * BN, p.N, k0, p.K, st + BM * NK, wv, lane);
+    } else {
+      la.issue((uint32_t)(((long)i_tm * BM * p.lda + k0) * 2), st);
+      lb.issue((uint32_t)(((long)i_tn * BN * p.ldb + k0) * 2), st + BM * NK);
+    }
+    if (++i_kt == nk) {
+      i_kt = 0;
+      ++i_round;
+      if (i_round < my_n) grouped_coords(tile_pid(i_round, G), nm, nn, i_tm, i_tn);
+    }
+  };
+  auto is_async = [&](int t) { return !(ragged && (t % nk) * NK + NK > p.K); };
+  // wait until stage t has landed, stages up to `last` issued
+  auto wait_stage = [&](int t, int last) {
+    int after = 0;
+    for (int u = t + 1; u <= last; ++u) after += is_async(u) ? 1 : 0;
+    if (after >= 2) wait_vmcnt<2 * PER>();
+    else if (after == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8 af[2][FM], bfr[2][FN];
+  auto load_frags = [&](int t, int ks, int set) {
+    const uint16_t* As = lds + (t % NS) * STAGE;
+    const uint16_t* Bs = As + BM * NK;
+    const int slot = (ks * 2 + g) ^ swz;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[set][i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + ((wm + i * 32 + fr) * 4 + slot) * 8));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[set][j] = __builtin_bit_cast(bf16x8, *(const uint4*)(Bs + ((wn + j * 32 + fr) * 4 + slot) * 8));
+  };
+  auto mfma_set = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Stage s + 1 is made visible (wait + barrier) one stage early, so the
+  // first fragments of the next stage are read before the barrier and only
+  // the barrier itself separates the two MFMA groups of a stage.
+  if (total > 0) {
+    const int pro = min(NS - 1, total);
+    for (int t = 0; t < pro; ++t) issue_next(t);
+    wait_stage(min(1, total - 1), pro - 1);
+    stage_barrier();
+    load_frags(0, 0, 0);
+  }
+  int s = 0;
+  for (int round = 0; round < my_n; ++round) {
+    for (int kt = 0; kt < nk; ++kt, ++s) {
+      if (s + NS - 1 < total) issue_next(s + NS - 1);
+      load_frags(s, 1, 1);
+      mfma_set(0);
+      if (s + 1 < total) load_frags(s + 1, 0, 0);
+      if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
+      stage_barrier();
+      mfma_set(1);
+    }
+    int tm, tn;
+    grouped_coords(tile_pid(round, G), nm, nn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          int r = m0 + wm + i * 32 + fr;
+          int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+          epi_store4<EPI>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                          acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      }
+  }
 }
 
 // ------------------------------------------------------------------ fp32 FMA kernel
@@ -447,8 +675,45 @@ static void launch_cfg(GP q, int S, hipStream_t st) {
   k_gemm_bf16<BM, BN, 2, 2, AT, BT, EPI><<<dim3(nb, 1, S), 256, 0, st>>>(q);
 }
 
+// NT tile choice: 256x256 (8 waves), 256x192 or 256x128 (4 waves), by the
+// number of 256-CU waves of tiles weighted with each shape's measured
+// relative throughput.
+static int plan_nt(int M, int N) {
+  const int bn[3] = {256, 192, 128};
+  const double eff[3] = {1.00, 0.93, 0.80};
+  int best = 0;
+  double bt = 1e30;
+  for (int c = 0; c < 3; ++c) {
+    long tiles = (long)cdiv(M, 256) * cdiv(N, bn[c]);
+    double t = (double)((tiles + 255) / 256) * bn[c] / 256.0 / eff[c];
+    if (t < bt - 1e-9) {
+      bt = t;
+      best = c;
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+static void launch_nt(GP q, hipStream_t st) {
+  int tiles = cdiv(q.M, BM) * cdiv(q.N, BN);
+  int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
+  k_gemm_nt<BM, BN, WM, WN, EPI><<<grid, WM * WN * 64, 0, st>>>(q);
+}
+
 template <bool AT, bool BT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
+  if constexpr (!AT && !BT && EPI != EPI_WGRAD) {
+    if (a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
+      p.kchunk = a.K;
+      switch (plan_nt(a.M, a.N)) {
+        case 0: launch_nt<256, 256, 4, 2, EPI>(p, st); break;
+        case 1: launch_nt<256, 192, 2, 2, EPI>(p, st); break;
+        default: launch_nt<256, 128, 2, 2, EPI>(p, st); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const bool wg = EPI == EPI_WGRAD && a.ldo == a.N && a.splitk_ws;
   Plan pl = plan_gemm(a.M, a.N, a.K, wg, wg ? a.splitk_ws_elems : 0);
   p.kchunk = pl.kchunk;
