@@ -819,6 +819,40 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow,
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ weight transpose
+// dst[c * ldt + r] = src[r * C + c] for a bf16 matrix src [R, C]: 64 x 64
+// tiles through LDS so both the reads and the writes are row-contiguous.
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int R,
+                                                        int C, uint16_t* __restrict__ dst, int ldt) {
+  __shared__ uint16_t t[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int i = ty; i < 64; i += 8) {
+    int r = r0 + i, c = c0 + 2 * tx;
+    uint32_t v = 0;
+    if (r < R && c + 1 < C) v = *(const uint32_t*)(src + (size_t)r * C + c);
+    else if (r < R && c < C) v = src[(size_t)r * C + c];
+    t[i][2 * tx] = (uint16_t)(v & 0xffffu);
+    t[i][2 * tx + 1] = (uint16_t)(v >> 16);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 8) {
+    int c = c0 + i, r = r0 + 2 * tx;
+    if (c >= C) continue;
+    if (r + 1 < R) {
+      *(uint32_t*)(dst + (size_t)c * ldt + r) = (uint32_t)t[2 * tx][i] | ((uint32_t)t[2 * tx + 1][i] << 16);
+    } else if (r < R) {
+      dst[(size_t)c * ldt + r] = t[2 * tx][i];
+    }
+  }
+}
+
+hipError_t transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, int ldt, hipStream_t st) {
+  if (ldt % 2) return hipErrorInvalidValue;
+  k_transpose_bf16<<<dim3(cdiv(C, 64), cdiv(R, 64)), 256, 0, st>>>(src, R, C, dst, ldt);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ misc
 __global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

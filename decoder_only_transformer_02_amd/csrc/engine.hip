@@ -118,12 +118,16 @@ struct gpt2_ctx {
   std::vector<ParamSpec> specs;
   std::vector<size_t> poff;  // element offset of each parameter in the flat arrays
   size_t nflat = 0;          // flat array length (padded)
+  size_t nflat_t = 0;        // transposed-copy array length
   int L, H, C, hd, V, Vp, ldl, maxM;
   bool bf;
   size_t act_es;  // activation element size
 
   float *params, *grads, *am, *av;
   uint16_t* shadow;
+  uint16_t* shadow_t;              // transposed bf16 copies of the GEMM weights
+  std::vector<size_t> toff;        // element offset of each transposed copy (or -1)
+  std::vector<int> tld;            // its row stride
   std::vector<float*> h, mean, rstd, lse;
   std::vector<void*> ln, qkv, att, fcu, fcg;
   void* logits;
@@ -152,6 +156,7 @@ struct gpt2_ctx {
   const void* W(int j) const {  // GEMM operand copy of a weight
     return bf ? (const void*)(shadow + poff[j]) : (const void*)(params + poff[j]);
   }
+  const void* Wt(int j) const { return shadow_t + toff[j]; }  // [in, out] (bf16 only)
   int li(int l, int k) const { return 2 + 12 * l + k; }  // parameter index in layer l
   void* act(void* base, size_t elems_off) const { return (char*)base + elems_off * act_es; }
 };
@@ -213,6 +218,17 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t o_par = pl.raw(nflat * 4), o_grad = pl.raw(nflat * 4);
   size_t o_m = pl.raw(nflat * 4), o_v = pl.raw(nflat * 4);
   size_t o_sh = bf ? pl.raw(nflat * 2) : 0;
+  std::vector<size_t> toff(specs.size(), (size_t)-1);
+  std::vector<int> tld(specs.size(), 0);
+  size_t nt = 0;
+  for (size_t j = 0; j < specs.size(); ++j) {
+    if (!bf || !specs[j].gemm_weight) continue;
+    int ld = (int)(((specs[j].rows + 63) / 64) * 64);   // transposed rows are the old columns
+    toff[j] = nt;
+    tld[j] = ld;
+    nt += (size_t)specs[j].cols * ld;
+  }
+  size_t o_sht = bf ? pl.raw(nt * 2 + 256) : 0;
   // tensor-table views of the flat arrays
   for (size_t j = 0; j < specs.size(); ++j) {
     auto& s = specs[j];
@@ -288,6 +304,10 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     x->params = (float*)(a + o_par); x->grads = (float*)(a + o_grad);
     x->am = (float*)(a + o_m); x->av = (float*)(a + o_v);
     x->shadow = bf ? (uint16_t*)(a + o_sh) : nullptr;
+    x->shadow_t = bf ? (uint16_t*)(a + o_sht) : nullptr;
+    x->toff = toff;
+    x->tld = tld;
+    x->nflat_t = nt;
     for (int k = 0; k <= 2 * L; ++k) {
       x->h.push_back((float*)(a + o_h[k]));
       x->ln.push_back(a + o_ln[k]);
@@ -438,13 +458,21 @@ hipError_t ln_backward(gpt2_ctx* c, int k, int wj, const void* dy, bool accum, f
                                   beta, c->st);
 }
 
+// dX[M, in] = dY[M, out] W[out, in]: NT against the transposed copy in bf16,
+// NN (B transposed in memory) in fp32.
+GemmArgs dx_args(gpt2_ctx* c, int M, int n_in, int n_out, const void* dY, int ldy, int wj, int kind,
+                 void* out, int ldo) {
+  if (c->bf)
+    return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->Wt(wj), c->tld[wj], false, kind, out, ldo);
+  return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->W(wj), n_in, true, kind, out, ldo);
+}
+
 // Backward of block l given dres (fp32) / dres_act = dL/d h[2l+2]; leaves
 // dL/d h[2l] in dres / dres_act.
 hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   const int C = c->C;
   // mlp projection: dg = dr W_mp, du = dg * gelu'(u); dW_mp = dr^T g; db_mp = sum dr
-  GemmArgs g = gemm_args(c, M, 4 * C, C, c->dres_act, C, false, c->W(c->li(l, 10)), 4 * C, true,
-                         gk::EPI_DGELU, c->du, 4 * C);
+  GemmArgs g = dx_args(c, M, 4 * C, C, c->dres_act, C, c->li(l, 10), gk::EPI_DGELU, c->du, 4 * C);
   g.aux = c->fcu[l];
   KCHK(run_gemm(c, g));
   g = gemm_args(c, C, 4 * C, M, c->dres_act, C, true, c->fcg[l], 4 * C, true, gk::EPI_WGRAD,
@@ -453,8 +481,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   KCHK(run_gemm(c, g));
   KCHK(gk::colsum(c->dres_act, c->bf, M, C, C, c->G(c->li(l, 11)), beta, c->col_part, c->st));
   // fc: da2 = du W_fc; dW_fc = du^T a2; db_fc = sum du
-  g = gemm_args(c, M, C, 4 * C, c->du, 4 * C, false, c->W(c->li(l, 8)), C, true, gk::EPI_STORE,
-                c->dA, C);
+  g = dx_args(c, M, C, 4 * C, c->du, 4 * C, c->li(l, 8), gk::EPI_STORE, c->dA, C);
   KCHK(run_gemm(c, g));
   g = gemm_args(c, 4 * C, C, M, c->du, 4 * C, true, c->ln[2 * l + 1], C, true, gk::EPI_WGRAD,
                 c->G(c->li(l, 8)), C);
@@ -463,8 +490,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   KCHK(gk::colsum(c->du, c->bf, M, 4 * C, 4 * C, c->G(c->li(l, 9)), beta, c->col_part, c->st));
   KCHK(ln_backward(c, 2 * l + 1, c->li(l, 6), c->dA, true, beta, M));
   // attention projection: do = dr W_proj; dW_proj = dr^T o; db_proj
-  g = gemm_args(c, M, C, C, c->dres_act, C, false, c->W(c->li(l, 4)), C, true, gk::EPI_STORE,
-                c->dattn, C);
+  g = dx_args(c, M, C, C, c->dres_act, C, c->li(l, 4), gk::EPI_STORE, c->dattn, C);
   KCHK(run_gemm(c, g));
   g = gemm_args(c, C, C, M, c->dres_act, C, true, c->att[l], C, true, gk::EPI_WGRAD,
                 c->G(c->li(l, 4)), C);
@@ -477,8 +503,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
                       c->hd, c->bf, c->st));
   }
   // qkv: da1 = dqkv W_qkv; dW_qkv = dqkv^T a1; db_qkv
-  g = gemm_args(c, M, C, 3 * C, c->dqkv, 3 * C, false, c->W(c->li(l, 2)), C, true, gk::EPI_STORE,
-                c->dA, C);
+  g = dx_args(c, M, C, 3 * C, c->dqkv, 3 * C, c->li(l, 2), gk::EPI_STORE, c->dA, C);
   KCHK(run_gemm(c, g));
   g = gemm_args(c, 3 * C, C, M, c->dqkv, 3 * C, true, c->ln[2 * l], C, true, gk::EPI_WGRAD,
                 c->G(c->li(l, 2)), C);
@@ -486,6 +511,18 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   KCHK(run_gemm(c, g));
   KCHK(gk::colsum(c->dqkv, c->bf, M, 3 * C, 3 * C, c->G(c->li(l, 3)), beta, c->col_part, c->st));
   KCHK(ln_backward(c, 2 * l, c->li(l, 0), c->dA, true, beta, M));
+  return hipSuccess;
+}
+
+// Refreshes the transposed bf16 copies from the bf16 weight copies.
+hipError_t refresh_transposed(gpt2_ctx* c) {
+  if (!c->bf) return hipSuccess;
+  for (size_t j = 0; j < c->specs.size(); ++j) {
+    if (c->toff[j] == (size_t)-1) continue;
+    const auto& sp = c->specs[j];
+    KCHK(gk::transpose_bf16(c->shadow + c->poff[j], (int)sp.rows, (int)sp.cols,
+                            c->shadow_t + c->toff[j], c->tld[j], c->st));
+  }
   return hipSuccess;
 }
 
@@ -617,6 +654,8 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
   if ((e = hipMemsetAsync(c->logits, 0, (size_t)c->maxM * c->ldl * c->act_es, c->st)))
     return bail(e, "zero logits");
   if (c->bf && (e = gk::to_bf16(c->params, c->shadow, c->nflat, c->st))) return bail(e, "bf16 copy");
+  if (c->bf && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
+  if ((e = refresh_transposed(c))) return bail(e, "transposed copies");
   // AdamW chunk table
   std::vector<gk::AdamChunk> ch;
   const size_t CH = 16384;
@@ -708,8 +747,7 @@ GPT2_API gpt2_status gpt2_backward(gpt2_ctx* c, float grad_scale) {
   const int B = c->B, T = c->T, M = B * T, C = c->C, L = c->L;
   const float beta = c->grads_fresh ? 0.f : 1.f;
   // classifier (tied): dhf = s dz wte ; dwte = s dz^T hf + beta dwte
-  GemmArgs g = gemm_args(c, M, C, c->Vp, c->logits, c->ldl, false, c->W(0), C, true, gk::EPI_STORE,
-                         c->dA, C);
+  GemmArgs g = dx_args(c, M, C, c->Vp, c->logits, c->ldl, 0, gk::EPI_STORE, c->dA, C);
   g.alpha = grad_scale;
   HIPCHK(c, run_gemm(c, g));
   g = gemm_args(c, c->Vp, C, M, c->logits, c->ldl, true, c->ln[2 * L], C, true, gk::EPI_WGRAD,
@@ -751,6 +789,7 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
     Timed t(c, GPT2_T_ADAMW);
     HIPCHK(c, gk::adamw(c->params, c->grads, c->am, c->av, c->shadow, c->chunks, c->nchunks, c->scal,
                         lr, c->cfg.beta1, c->cfg.beta2, c->cfg.adam_eps, c->cfg.weight_decay, c->st));
+    HIPCHK(c, refresh_transposed(c));
   }
   c->armed_step = false;
   c->grads_fresh = true;

@@ -744,7 +744,8 @@ static hipError_t launch_f32(const GemmArgs& a, GP p, hipStream_t st) {
 // with the store / GELU-derivative epilogues; dW as TN (both transposed).
 template <int EPI>
 static hipError_t dispatch_t(const GemmArgs& a, const GP& p, hipStream_t st) {
-  constexpr bool NT_OK = EPI == EPI_STORE || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr bool NT_OK = EPI == EPI_STORE || EPI == EPI_LOGITS || EPI == EPI_GELU || EPI == EPI_RESID ||
+                        EPI == EPI_DGELU;
   constexpr bool NN_OK = EPI == EPI_STORE || EPI == EPI_DGELU;
   constexpr bool TN_OK = EPI == EPI_WGRAD;
   if (a.bf16) {

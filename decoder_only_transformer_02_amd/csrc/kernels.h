@@ -60,6 +60,8 @@ struct AdamChunk {
 hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow,
                  const AdamChunk* chunks, int nchunks, const float* scal, float lr, float beta1,
                  float beta2, float eps, float wd, hipStream_t st);
+// dst[c * ldt + r] = src[r * C + c] for a bf16 [R, C] matrix (ldt even).
+hipError_t transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, int ldt, hipStream_t st);
 // bf16 copy of n fp32 values (RNE).
 hipError_t to_bf16(const float* x, uint16_t* y, size_t n, hipStream_t st);
 hipError_t fill_f32(float* x, size_t n, float v, hipStream_t st);
