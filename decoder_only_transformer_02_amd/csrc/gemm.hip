@@ -29,7 +29,8 @@ struct GP {
   const void* aux;
   const float* bias;
   float alpha, beta;
-  int kchunk;  // split-K: K range per blockIdx.z (multiple of the K tile)
+  int kchunk;  // split-K: K range per split (multiple of the K tile)
+  int splits;  // TN kernel: number of K splits (1: write the output directly)
 };
 
 // ------------------------------------------------------------------ epilogues
@@ -558,6 +559,209 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 TN kernel (weight gradients)
+// D[r][c] = sum_m A[m * lda + r] * B[m * ldb + c]: both operands keep their
+// natural [token][feature] layout.  Stages of 32 tokens are loaded straight
+// into LDS (buffer loads, tokens past M read as zero, so a ragged token
+// count needs no special path) as [m][cols] tiles whose 16-byte chunk p of
+// row m sits at p ^ 4 (m % 4); MFMA operands are built with the LDS
+// transpose read (ds_read_b64_tr_b16): each 16-lane group reads a 4 x 16
+// (token x feature) block and lane i receives the 4 tokens of feature i, so
+// two reads give the 8 k values of a 32x32x16 operand.  The swizzle keeps
+// the two 16-lane groups that share a cycle on all 64 banks.
+constexpr int TK = 32;  // tokens per stage
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+template <int COLS, int NW>
+struct TokLoader {
+  static constexpr int CPR = COLS / 8;      // 16-byte chunks per token row
+  static constexpr int NI = TK * CPR / 64 / NW;
+  static_assert(CPR >= 16 && NI * 64 * NW == TK * CPR, "tile width must be >= 128, split evenly");
+  void* base;
+  uint32_t nbytes;
+  uint32_t voff[NI];
+  int blk0;
+  __device__ __forceinline__ void init(const void* b, long ld, int M, int wv, int lane) {
+    uint64_t bytes = (uint64_t)M * ld * 2;
+    base = const_cast<void*>(b);
+    nbytes = (uint32_t)(bytes > 0xffffffffull ? 0xffffffffull : bytes);
+    blk0 = wv * NI;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int lin = (blk0 + i) * 64 + lane;   // LDS chunk slot
+      const int m = lin / CPR, slot = lin % CPR;
+      const int pch = slot ^ (4 * (m & 3));     // global chunk stored in this slot
+      voff[i] = (uint32_t)((long)m * ld * 2 + pch * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t soff, uint16_t* lds_op) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) buffer_load_lds16(base, nbytes, lds_op + (blk0 + i) * 512, voff[i], soff);
+  }
+};
+
+// 8 k values (tokens ks*16 + 8g .. +7) of feature column `col` of an LDS tile
+// [32][COLS], as an MFMA operand; lane l serves column base + l % 32.
+template <int COLS>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int cbase, int ks, int lane) {
+  const int G = lane >> 4, q = lane & 15;
+  const int col = cbase + 16 * (G & 1) + 4 * (q & 3);
+  v4s h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int m = ks * 16 + 8 * (G >> 1) + 4 * hh + (q >> 2);
+    const int off = m * COLS + (((col >> 3) ^ (4 * (m & 3))) << 3) + (col & 7);
+    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
+                                                 __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
+                                                 __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
+                                                 __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]})));
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int STAGE = (BM + BN) * TK;
+  constexpr int PER = TokLoader<BM, NW>::NI + TokLoader<BN, NW>::NI;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = (wv / WN) * TM, wn = (wv % WN) * TN;
+  const int fr = lane & 31, g = lane >> 5;
+  const int nm = cdiv(p.M, BM), nn = cdiv(p.N, BN);
+  const int tiles = nm * nn;
+  const int S = p.splits;
+  const int items = tiles * S;
+  const int G = gridDim.x;
+  int my_n = 0;
+  while (tile_pid(my_n, G) < items) ++my_n;
+
+  TokLoader<BM, NW> la;
+  TokLoader<BN, NW> lb;
+  la.init(p.A, p.lda, p.K, wv, lane);
+  lb.init(p.B, p.ldb, p.K, wv, lane);
+
+  auto item_nk = [&](int z) {
+    const int kb = z * p.kchunk;
+    return cdiv(min(p.K, kb + p.kchunk) - kb, TK);
+  };
+  // issue cursor
+  int i_round = 0, i_kt = 0, i_tm = 0, i_tn = 0, i_z = 0, i_nk = 0;
+  auto set_item = [&](int round, int& tm, int& tn, int& z) {
+    const int pid = tile_pid(round, G);
+    z = pid / tiles;
+    grouped_coords(pid % tiles, nm, nn, tm, tn);
+  };
+  int total = 0;
+  for (int r = 0; r < my_n; ++r) {
+    int tm, tn, z;
+    set_item(r, tm, tn, z);
+    total += item_nk(z);
+  }
+  if (my_n > 0) {
+    set_item(0, i_tm, i_tn, i_z);
+    i_nk = item_nk(i_z);
+  }
+  auto issue_next = [&](int t) {
+    uint16_t* st = lds + (t % NS) * STAGE;
+    const int m0 = i_z * p.kchunk + i_kt * TK;
+    la.issue((uint32_t)(((long)m0 * p.lda + i_tm * BM) * 2), st);
+    lb.issue((uint32_t)(((long)m0 * p.ldb + i_tn * BN) * 2), st + BM * TK);
+    if (++i_kt == i_nk) {
+      i_kt = 0;
+      if (++i_round < my_n) {
+        set_item(i_round, i_tm, i_tn, i_z);
+        i_nk = item_nk(i_z);
+      }
+    }
+  };
+  auto wait_stage = [&](int t, int last) {
+    const int after = last - t;
+    if (after >= 2) wait_vmcnt<2 * PER>();
+    else if (after == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8 af[2][FM], bfr[2][FN];
+  auto load_frags = [&](int t, int ks, int set) {
+    const uint16_t* As = lds + (t % NS) * STAGE;
+    const uint16_t* Bs = As + BM * TK;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[set][i] = tr_frag<BM>(As, wm + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[set][j] = tr_frag<BN>(Bs, wn + j * 32, ks, lane);
+  };
+  auto mfma_set = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+  };
+
+  if (total > 0) {
+    const int pro = min(NS - 1, total);
+    for (int t = 0; t < pro; ++t) issue_next(t);
+    wait_stage(min(1, total - 1), pro - 1);
+    stage_barrier();
+    load_frags(0, 0, 0);
+  }
+  int s = 0;
+  for (int round = 0; round < my_n; ++round) {
+    int tm, tn, z;
+    set_item(round, tm, tn, z);
+    const int nk = item_nk(z);
+    for (int kt = 0; kt < nk; ++kt, ++s) {
+      if (s + NS - 1 < total) issue_next(s + NS - 1);
+      load_frags(s, 1, 1);
+      mfma_set(0);
+      if (s + 1 < total) load_frags(s + 1, 0, 0);
+      if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
+      stage_barrier();
+      mfma_set(1);
+    }
+    const int m0 = tm * BM, n0 = tn * BN;
+    float* op = (float*)p.out + (S > 1 ? (size_t)z * p.M * p.ldo : 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int r = m0 + wm + i * 32 + fr;
+          const int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+          if (r < p.M && c < p.N) {   // N % 4 == 0
+            float4 v = make_float4(acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2],
+                                   acc[i][j][e4 * 4 + 3]);
+            float* dst = op + (size_t)r * p.ldo + c;
+            if (S == 1) {
+              v.x *= p.alpha; v.y *= p.alpha; v.z *= p.alpha; v.w *= p.alpha;
+              if (p.beta != 0.f) {
+                float4 o = *(const float4*)dst;
+                v.x += p.beta * o.x; v.y += p.beta * o.y; v.z += p.beta * o.z; v.w += p.beta * o.w;
+              }
+            }
+            *(float4*)dst = v;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 FMA kernel
 template <bool AT, bool BT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(GP p) {
@@ -664,9 +868,51 @@ static Plan plan_gemm(int M, int N, int K, bool wgrad, size_t ws_elems) {
   return best;
 }
 
+// Weight-gradient (TN) tile / split-K choice: 256x256 (8 waves), 256x128,
+// 128x128 (two per CU); MFMA time of the workgroup waves at each shape's
+// measured relative throughput plus the HBM time of the split partials.
+struct TnPlan {
+  int cfg, splits, kchunk;
+};
+static TnPlan plan_tn(int M, int N, int K, size_t ws_elems) {
+  const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128}, per_cu[3] = {1, 1, 2};
+  const double eff[3] = {1.0, 0.65, 0.55};
+  const double cu_flops = 2.5e15 / 256.0, hbm = 6.0e12;
+  TnPlan best{2, 1, cdiv(K, TK) * TK};
+  double bt = 1e30;
+  for (int c = 0; c < 3; ++c) {
+    long tiles = (long)cdiv(M, bm[c]) * cdiv(N, bn[c]);
+    for (int S = 1; S <= 32; ++S) {
+      int kchunk = cdiv(cdiv(K, S), TK) * TK;
+      if (cdiv(K, kchunk) != S) continue;
+      if (S > 1 && (size_t)S * M * N > ws_elems) continue;
+      long slots = 256L * per_cu[c];
+      long waves = (tiles * S + slots - 1) / slots;
+      double t = waves * per_cu[c] * (2.0 * bm[c] * bn[c] * kchunk) / (cu_flops * eff[c]);
+      if (S > 1) t += ((double)S + 2.0) * M * N * 4.0 / hbm + 3e-6;
+      if (t < bt) {
+        bt = t;
+        best = TnPlan{c, S, kchunk};
+      }
+    }
+  }
+  return best;
+}
+
 size_t gemm_splitk_ws_elems(int M, int N, int K) {
   Plan pl = plan_gemm(M, N, K, true, (size_t)-1);
-  return pl.splits > 1 ? (size_t)pl.splits * M * N : 0;
+  size_t a = pl.splits > 1 ? (size_t)pl.splits * M * N : 0;
+  TnPlan tp = plan_tn(M, N, K, (size_t)-1);
+  size_t b = tp.splits > 1 ? (size_t)tp.splits * M * N : 0;
+  return a > b ? a : b;
+}
+
+template <int BM, int BN, int WM, int WN>
+static void launch_tn(GP q, int per_cu, hipStream_t st) {
+  long items = (long)cdiv(q.M, BM) * cdiv(q.N, BN) * q.splits;
+  long cap = 256L * per_cu;
+  int grid = (int)(items < cap ? ((items + 7) / 8) * 8 : cap);
+  k_gemm_tn<BM, BN, WM, WN><<<grid, WM * WN * 64, 0, st>>>(q);
 }
 
 template <int BM, int BN, bool AT, bool BT, int EPI>
@@ -703,6 +949,25 @@ static void launch_nt(GP q, hipStream_t st) {
 
 template <bool AT, bool BT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
+  if constexpr (AT && BT && EPI == EPI_WGRAD) {
+    if (a.N % 4 == 0 && a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws) {
+      TnPlan tp = plan_tn(a.M, a.N, a.K, a.splitk_ws_elems);
+      p.kchunk = tp.kchunk;
+      p.splits = tp.splits;
+      GP q = p;
+      if (tp.splits > 1) q.out = a.splitk_ws;
+      switch (tp.cfg) {
+        case 0: launch_tn<256, 256, 4, 2>(q, 1, st); break;
+        case 1: launch_tn<256, 128, 2, 2>(q, 1, st); break;
+        default: launch_tn<128, 128, 2, 2>(q, 2, st); break;
+      }
+      if (tp.splits > 1) {
+        size_t n = (size_t)a.M * a.N;
+        k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, tp.splits, n, (float*)a.out, a.alpha, a.beta);
+      }
+      return hipGetLastError();
+    }
+  }
   if constexpr (!AT && !BT && EPI != EPI_WGRAD) {
     if (a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
       p.kchunk = a.K;
@@ -772,7 +1037,7 @@ hipError_t gemm(const GemmArgs& a, hipStream_t st) {
   p.M = a.M; p.N = a.N; p.K = a.K;
   p.A = a.A; p.lda = a.lda; p.B = a.B; p.ldb = a.ldb;
   p.out = a.out; p.ldo = a.ldo; p.out2 = a.out2; p.aux = a.aux; p.bias = a.bias;
-  p.alpha = a.alpha; p.beta = a.beta; p.kchunk = a.K;
+  p.alpha = a.alpha; p.beta = a.beta; p.kchunk = a.K; p.splits = 1;
   switch (a.kind) {
     case EPI_STORE: return dispatch_t<EPI_STORE>(a, p, st);
     case EPI_LOGITS: return dispatch_t<EPI_LOGITS>(a, p, st);
