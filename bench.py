@@ -117,7 +117,7 @@ def main():
         "mfu": round(mfu, 4),
         "flops_per_token": fpt,
         "loss": round(loss, 5),
-        "roofline": {"kernel": "classifier GEMM forward (k_gemm_bf16, EPI_LOGITS)",
+        "roofline": {"kernel": "classifier GEMM forward (k_gemm_nt, EPI_LOGITS)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
                      "traffic": None, "avg_launch_ms": round(avg_k * 1e3, 4),
