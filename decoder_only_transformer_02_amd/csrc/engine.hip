@@ -803,6 +803,16 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
   return GPT2_OK;
 }
 
+GPT2_API double gpt2_lr_at(int64_t it, double max_lr, double min_lr, int64_t warmup,
+                          int64_t decay_end) {
+  if (it < 0 || warmup < 1 || decay_end <= warmup || !(min_lr >= 0.0) || !(max_lr >= min_lr))
+    return std::nan("");
+  if (it < warmup) return max_lr * (double)(it + 1) / (double)warmup;
+  if (it > decay_end) return min_lr;
+  const double f = (double)(it - warmup) / (double)(decay_end - warmup);
+  return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + std::cos(M_PI * f));
+}
+
 GPT2_API gpt2_status gpt2_block_fwd_bwd(gpt2_ctx* c, int32_t layer, const float* d_x,
                                         const float* d_dy, float* d_y, float* d_dx, int32_t B,
                                         int32_t T) {

@@ -27,7 +27,7 @@ TIMING = {"none": 0, "lmhead_fwd": 1, "gemm": 2, "attn_fwd": 3, "attn_bwd": 4, "
 # every symbol declared in include/gpt2.h
 EXPORTS = ["gpt2_default_config", "gpt2_arena_bytes", "gpt2_num_params", "gpt2_init_host",
            "gpt2_create", "gpt2_destroy", "gpt2_last_error", "gpt2_forward", "gpt2_backward",
-           "gpt2_zero_grad", "gpt2_step", "gpt2_block_fwd_bwd", "gpt2_num_tensors",
+           "gpt2_zero_grad", "gpt2_step", "gpt2_lr_at", "gpt2_block_fwd_bwd", "gpt2_num_tensors",
            "gpt2_tensor_info", "gpt2_timing_enable", "gpt2_timing_read"]
 
 
@@ -76,6 +76,7 @@ def lib():
         "gpt2_backward": (I32, [P, F]),
         "gpt2_zero_grad": (I32, [P]),
         "gpt2_step": (I32, [P, F, F, ct.POINTER(F)]),
+        "gpt2_lr_at": (ct.c_double, [I64, ct.c_double, ct.c_double, I64, I64]),
         "gpt2_block_fwd_bwd": (I32, [P, I32, P, P, P, P, I32, I32]),
         "gpt2_num_tensors": (I32, [P]),
         "gpt2_tensor_info": (I32, [P, I32, ct.POINTER(TensorDesc)]),
@@ -98,6 +99,12 @@ def make_config(n_layer, n_head, n_embd, block_size, vocab_size, padded_vocab, m
     c.block_size, c.vocab_size, c.padded_vocab = block_size, vocab_size, padded_vocab
     c.compute = GPT2_BF16 if compute == "bf16" else GPT2_FP32
     return c
+
+
+def lr_at(it: int, max_lr: float = 6e-4, min_lr: float = 6e-5, warmup: int = 132,
+          decay_end: int = 3400) -> float:
+    """Learning rate at optimizer iteration `it` (include/gpt2.h, gpt2_lr_at)."""
+    return lib().gpt2_lr_at(it, max_lr, min_lr, warmup, decay_end)
 
 
 def init_host(cfg: Config, seed: int) -> np.ndarray:

@@ -157,6 +157,20 @@ gpt2_status gpt2_zero_grad(gpt2_ctx* c);
  * is then reported as GPT2_E_NONFINITE. */
 gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_norm);
 
+/* Learning rate at optimizer iteration it (0-based), "Let's reproduce GPT-2
+ * (124M)" key takeaways, bullet "Optimization Hyperparameters" (linear
+ * warm-up, then cosine decay to 10 % of the maximum) with the iteration
+ * counts of "From Scratch: Building GPT-2 for Efficient Language Modeling",
+ * Training Setup table (132 warm-up, 3400 iterations):
+ *   it < warmup:                 max_lr * (it + 1) / warmup
+ *   warmup <= it <= decay_end:   min_lr + (max_lr - min_lr) * (1 + cos(pi f)) / 2,
+ *                                f = (it - warmup) / (decay_end - warmup)
+ *   it > decay_end:              min_lr
+ * so lr(warmup) = max_lr and lr(decay_end) = min_lr.  Host arithmetic in
+ * double precision; makes no HIP call.  Returns NaN when it < 0,
+ * warmup < 1, decay_end <= warmup, or not 0 <= min_lr <= max_lr. */
+double gpt2_lr_at(int64_t it, double max_lr, double min_lr, int64_t warmup, int64_t decay_end);
+
 /* One transformer block in isolation: y = block_layer(x) and dx, with the
  * block's parameter gradients written (overwritten) in the arena, for
  * upstream gradient dy.  d_x, d_dy, d_y, d_dx: device float32 [B,T,C]. */

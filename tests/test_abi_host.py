@@ -70,3 +70,18 @@ def test_host_init_equals_oracle_init(preset):
     diff = np.abs(got - flat)
     assert np.all(diff <= ulp), float((diff / np.maximum(ulp, 1e-45)).max())
     assert np.mean(got == flat) > 0.9999
+
+
+def test_lr_schedule_equals_oracle():
+    """The library's learning-rate schedule (host arithmetic) against the
+    oracle's at every iteration of the pages' run and past its end, plus
+    the closed-form values and the invalid-argument results."""
+    for it in range(0, 3600):
+        assert G.lr_at(it) == pytest.approx(O.lr_at(it), rel=1e-13, abs=0.0), it
+    assert G.lr_at(132) == 6e-4
+    assert G.lr_at(0) == pytest.approx(6e-4 / 132, rel=1e-15)
+    assert G.lr_at(3400) == pytest.approx(6e-5, rel=1e-15)
+    assert G.lr_at(10**9) == 6e-5
+    for bad in ((-1, 6e-4, 6e-5, 132, 3400), (0, 6e-4, 6e-5, 0, 3400),
+                (0, 6e-4, 6e-5, 132, 132), (0, 6e-5, 6e-4, 132, 3400), (0, 6e-4, -1.0, 132, 3400)):
+        assert np.isnan(G.lr_at(*bad)), bad
