@@ -100,6 +100,10 @@ bool config_ok(const gpt2_config* c, std::string* why) {
   if (c->max_batch < 1 || (int64_t)c->max_batch * c->max_seq > 32768)
     return bad("max_batch * max_seq must be in [1, 32768]");
   if (c->compute != GPT2_FP32 && c->compute != GPT2_BF16) return bad("bad compute mode");
+  // the GEMM operand loads address the logits with 32-bit byte offsets
+  const uint64_t ldl = ((uint64_t)c->padded_vocab + 63) / 64 * 64;
+  if ((uint64_t)c->max_batch * c->max_seq * ldl * (c->compute == GPT2_BF16 ? 2u : 4u) >= (1ull << 32))
+    return bad("logits buffer of 4 GiB or more");
   return true;
 }
 

@@ -72,8 +72,10 @@ typedef struct {
   int32_t n_embd;        /* C, multiple of 64, <= 1024 */
   int32_t block_size;    /* rows of the position embedding */
   int32_t vocab_size;    /* V: ids and targets must lie in [0, V) */
-  int32_t padded_vocab;  /* Vp >= V: rows of wte = width of the logits */
-  int32_t max_batch;     /* arena sizing: B * T <= max_batch * max_seq */
+  int32_t padded_vocab;  /* Vp >= V, <= 65536: rows of wte = width of the logits */
+  int32_t max_batch;     /* arena sizing: B * T <= max_batch * max_seq <= 32768,
+                            and the logits buffer (max_batch * max_seq rows of
+                            Vp rounded up to 64, 2 or 4 bytes each) < 4 GiB */
   int32_t max_seq;       /* T <= max_seq <= block_size */
   int32_t compute;       /* gpt2_compute */
   float ln_eps;          /* 1e-5 */

@@ -46,6 +46,12 @@ def test_arena_sizes_and_bad_configs():
     bad = _cfg(PRESETS["tiny"])
     bad.max_seq = bad.block_size + 1
     assert lib.gpt2_arena_bytes(ct.byref(bad)) == 0
+    # logits of 4 GiB or more are refused (32-bit buffer offsets); just below is fine
+    big = _cfg(PRESETS["gpt2_124m"], max_batch=32, max_seq=1024)
+    big.padded_vocab = 65536
+    assert lib.gpt2_arena_bytes(ct.byref(big)) == 0
+    big.padded_vocab = 65472
+    assert lib.gpt2_arena_bytes(ct.byref(big)) > 0
     # create refuses a NULL / misaligned / small arena before touching the GPU
     ctx = ct.c_void_p()
     good = _cfg(PRESETS["tiny"])
