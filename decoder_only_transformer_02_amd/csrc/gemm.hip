@@ -360,19 +360,24 @@ __device__ __forceinline__ void stage_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from base + voff + soff (range-checked against nbytes,
-// zero outside) into LDS at lds + 16 * lane.
+// 16 bytes per lane from base + soff + voff into LDS at lds + 16 * lane.
+// The descriptor starts at base + soff and holds the nbytes - soff bytes
+// that remain of the operand (soff < nbytes), so the hardware range check
+// sees only the per-lane offset: a lane whose bytes lie past the operand's
+// end reads zero, whatever the check does with a scalar offset.
 __device__ __attribute__((always_inline)) inline void buffer_load_lds16(void* base, uint32_t nbytes,
                                                                        uint16_t* lds, uint32_t voff,
                                                                        uint32_t soff) {
-  auto rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)nbytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, soff, 0, 0);
+  auto rsrc = __builtin_amdgcn_make_buffer_rsrc((char*)base + soff, (short)0, (int)(nbytes - soff),
+                                                0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
 // One operand's stage loads: NI buffer loads of 16 bytes per lane per stage,
 // each filling one 16-row block of the LDS tile.  The per-lane byte offsets
-// are loop invariant; the tile row and k position move in the scalar offset.
-// Rows past the end of the operand read as zero (buffer range check).
+// are loop invariant; the tile row and k position move the descriptor base.
+// Rows past the end of the operand read as zero (range check of the per-lane
+// offset against the bytes left after the stage's start).
 template <int ROWS, int NW>
 struct BufLoader {
   static constexpr int NI = ROWS * 4 / 64 / NW;  // 16-row blocks per wave per stage
@@ -562,8 +567,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
 // ------------------------------------------------------------------ bf16 TN kernel (weight gradients)
 // D[r][c] = sum_m A[m * lda + r] * B[m * ldb + c]: both operands keep their
 // natural [token][feature] layout.  Stages of 32 tokens are loaded straight
-// into LDS (buffer loads, tokens past M read as zero, so a ragged token
-// count needs no special path) as [m][cols] tiles whose 16-byte chunk p of
+// into LDS (buffer loads whose descriptor starts at the stage's first token,
+// so tokens past the last one fail the range check of the per-lane offset
+// and read as zero: a ragged token count needs no special path) as
+// [m][cols] tiles whose 16-byte chunk p of
 // row m sits at p ^ 4 (m % 4); MFMA operands are built with the LDS
 // transpose read (ds_read_b64_tr_b16): each 16-lane group reads a 4 x 16
 // (token x feature) block and lane i receives the 4 tokens of feature i, so
