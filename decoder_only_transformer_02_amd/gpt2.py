@@ -54,14 +54,9 @@ class GPT2Error(RuntimeError):
 _lib = None
 
 
-def lib():
-    """Loads libgpt2mi.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
-    L = ct.CDLL(LIB_PATH)
+def bind(L):
+    """Sets the argument and result types of every call in include/gpt2.h on
+    a loaded library handle."""
     P, I32, I64, SZ, F = ct.c_void_p, ct.c_int32, ct.c_int64, ct.c_size_t, ct.c_float
     cfgp = ct.POINTER(Config)
     sig = {
@@ -87,8 +82,18 @@ def lib():
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
     return L
+
+
+def lib():
+    """Loads libgpt2mi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    _lib = bind(ct.CDLL(LIB_PATH))
+    return _lib
 
 
 def make_config(n_layer, n_head, n_embd, block_size, vocab_size, padded_vocab, max_batch, max_seq,
@@ -125,7 +130,7 @@ class GPT2Step:
         self.torch = torch
         self.cfg = cfg
         self.device = torch.device(device)
-        L = lib()
+        self._L = L = lib()
         nbytes = L.gpt2_arena_bytes(ct.byref(cfg))
         if nbytes == 0:
             raise GPT2Error(GPT2_E_ARG, "invalid config")
@@ -140,7 +145,7 @@ class GPT2Step:
         self._tables()
 
     def _tables(self):
-        L = lib()
+        L = self._L
         self.tensors = {}
         d = TensorDesc()
         for i in range(L.gpt2_num_tensors(self.ctx)):
@@ -151,7 +156,7 @@ class GPT2Step:
 
     def close(self):
         if getattr(self, "ctx", None):
-            lib().gpt2_destroy(self.ctx)
+            self._L.gpt2_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):
@@ -162,28 +167,28 @@ class GPT2Step:
 
     def _check(self, st):
         if st != 0:
-            msg = lib().gpt2_last_error(self.ctx) if getattr(self, "ctx", None) else b""
+            msg = self._L.gpt2_last_error(self.ctx) if getattr(self, "ctx", None) else b""
             raise GPT2Error(st, (msg or b"").decode())
 
     # ------------------------------------------------------------------ calls
     def forward(self, tokens, targets=None, sync=True):
         B, T = tokens.shape
         loss = ct.c_float(0.0)
-        st = lib().gpt2_forward(self.ctx, ct.c_void_p(tokens.data_ptr()),
+        st = self._L.gpt2_forward(self.ctx, ct.c_void_p(tokens.data_ptr()),
                                 ct.c_void_p(targets.data_ptr()) if targets is not None else None,
                                 B, T, ct.byref(loss) if sync else None)
         self._check(st)
         return loss.value if (sync and targets is not None) else None
 
     def backward(self, grad_scale=1.0):
-        self._check(lib().gpt2_backward(self.ctx, grad_scale))
+        self._check(self._L.gpt2_backward(self.ctx, grad_scale))
 
     def zero_grad(self):
-        self._check(lib().gpt2_zero_grad(self.ctx))
+        self._check(self._L.gpt2_zero_grad(self.ctx))
 
     def step(self, lr, clip=1.0, sync=True):
         norm = ct.c_float(0.0)
-        self._check(lib().gpt2_step(self.ctx, lr, clip, ct.byref(norm) if sync else None))
+        self._check(self._L.gpt2_step(self.ctx, lr, clip, ct.byref(norm) if sync else None))
         return norm.value if sync else None
 
     def block_fwd_bwd(self, layer, x, dy):
@@ -191,18 +196,18 @@ class GPT2Step:
         B, T, C = x.shape
         y = self.torch.empty_like(x)
         dx = self.torch.empty_like(x)
-        self._check(lib().gpt2_block_fwd_bwd(self.ctx, layer, ct.c_void_p(x.data_ptr()),
+        self._check(self._L.gpt2_block_fwd_bwd(self.ctx, layer, ct.c_void_p(x.data_ptr()),
                                              ct.c_void_p(dy.data_ptr()), ct.c_void_p(y.data_ptr()),
                                              ct.c_void_p(dx.data_ptr()), B, T))
         return y, dx
 
     def timing_enable(self, kernel_class: str):
-        self._check(lib().gpt2_timing_enable(self.ctx, TIMING[kernel_class]))
+        self._check(self._L.gpt2_timing_enable(self.ctx, TIMING[kernel_class]))
 
     def timing_read(self):
         ms = ct.c_double(0.0)
         n = ct.c_int64(0)
-        self._check(lib().gpt2_timing_read(self.ctx, ct.byref(ms), ct.byref(n)))
+        self._check(self._L.gpt2_timing_read(self.ctx, ct.byref(ms), ct.byref(n)))
         return ms.value, n.value
 
     # ------------------------------------------------------------------ views

@@ -1,0 +1,81 @@
+"""ctypes binding of the CPU emulation of the HIP library (tests only).
+
+EmuStep has the interface of the product binding's GPT2Step, but its arena
+is host memory (a torch CPU tensor) and its calls go to
+_build/emu/libgpt2mi_emu.so, the same kernel and engine sources compiled for
+the host by build_emu.py.  `kernels()` gives the direct single-kernel entry
+points of kernel_entry.cpp.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+
+import numpy as np
+import torch
+
+from decoder_only_transformer_02_amd import gpt2 as G
+from tests.emu import build_emu
+
+_emu = None
+
+
+def emu_lib():
+    global _emu
+    if _emu is None:
+        L = G.bind(ct.CDLL(build_emu.build()))
+        P, I, F, SZ = ct.c_void_p, ct.c_int, ct.c_float, ct.c_size_t
+        sig = {
+            "emu_set_range_mode": (None, [I]),
+            "emu_set_reverse_order": (None, [I]),
+            "emu_collectives": (ct.c_long, []),
+            "emu_gemm": (I, [I, I, I, P, I, I, P, I, I, I, P, I, P, P, P, F, F, I, P, SZ]),
+            "emu_gemm_splitk_ws_elems": (SZ, [I, I, I]),
+            "emu_attn_fwd": (I, [P, P, P, I, I, I, I, I]),
+            "emu_attn_bwd_ws": (SZ, [I, I, I]),
+            "emu_attn_bwd": (I, [P, P, P, P, P, P, I, I, I, I, I]),
+            "emu_xent": (I, [P, I, I, I, I, P, P, F, I, I, P]),
+            "emu_embed_bwd_ws": (SZ, [I, I]),
+            "emu_embed_bwd": (I, [P, P, P, P, I, I, I, I, I, F, P]),
+            "emu_ln_fwd": (I, [P, P, P, P, I, P, P, I, I, F]),
+            "emu_ln_bwd_part_floats": (I, [I, I]),
+            "emu_ln_bwd": (I, [P, P, P, P, P, I, P, P, I, P, I, I, P, P, F]),
+            "emu_colsum_parts": (I, [I]),
+            "emu_colsum": (I, [P, I, I, I, I, P, F, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _emu = L
+    return _emu
+
+
+def ptr(t) -> ct.c_void_p:
+    """Address of a torch tensor or numpy array (host memory)."""
+    if isinstance(t, np.ndarray):
+        return ct.c_void_p(t.ctypes.data)
+    return ct.c_void_p(t.data_ptr())
+
+
+class EmuStep(G.GPT2Step):
+    """GPT2Step on the emulated library with a host-memory arena."""
+
+    def __init__(self, cfg: G.Config, seed: int = 0, device=None):
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device("cpu")
+        self._L = L = emu_lib()
+        nbytes = L.gpt2_arena_bytes(ct.byref(cfg))
+        if nbytes == 0:
+            raise G.GPT2Error(G.GPT2_E_ARG, "invalid config")
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8)
+        off = (-raw.data_ptr()) % 256
+        self._raw = raw
+        self.arena = raw[off:off + nbytes]
+        ctx = ct.c_void_p()
+        st = L.gpt2_create(ct.byref(cfg), ct.c_uint64(seed), ct.c_void_p(self.arena.data_ptr()), nbytes,
+                           None, ct.byref(ctx))
+        if st != 0:
+            raise G.GPT2Error(st, "gpt2_create")
+        self.ctx = ctx
+        self._tables()

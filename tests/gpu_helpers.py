@@ -1,6 +1,7 @@
-"""Shared helpers of the GPU parity tests: configuration pairs for the
-library and the oracle, running one step through the C ABI, and the
-comparison measures."""
+"""Shared helpers of the parity tests: configuration pairs for the library
+and the oracle, running one step through the C ABI on a backend (the HIP
+library on the GPU, or its CPU emulation), and the comparison measures with
+the tolerances of the two arithmetic paths."""
 from __future__ import annotations
 
 import functools
@@ -34,6 +35,24 @@ def oracle_init(oc: O.Config, seed: int):
 def to_dev(a):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+class Backend:
+    """Where the library runs: `make(cfg, seed)` returns a GPT2Step-like
+    context and `dev(array)` moves an input array to that backend."""
+
+    def __init__(self, name, make, dev):
+        self.name, self.make, self.dev = name, make, dev
+
+
+GPU = Backend("gpu", lambda cfg, seed: G.GPT2Step(cfg, seed=seed), to_dev)
+
+
+def emu_backend() -> Backend:
+    import torch
+    from tests.emu.binding import EmuStep
+    return Backend("emu", lambda cfg, seed: EmuStep(cfg, seed=seed),
+                   lambda a: torch.from_numpy(np.ascontiguousarray(a)))
 
 
 def gpu_grads(m: G.GPT2Step, names):
@@ -78,3 +97,60 @@ def check_post_adamw(new_gpu, new_ref, g_gpu, g_ref, lr, exact: bool):
             assert d[same].max() <= 1e-3, (n, d[same].max())
         assert d.max() <= 2 * lr + 1e-4, (n, d.max())
     return flips / max(total, 1)
+
+
+def stream_for(p, n, seed):
+    if p["tokens"] == "zipf":
+        return inputs.zipf_stream(seed, n, p["vocab_size"])
+    return inputs.uniform_stream(seed, n, p["vocab_size"])
+
+
+def run_step(p, B, T, seed=0, data_seed=1, lr=6e-4, dt=np.float64, micro=1, be: Backend = GPU):
+    """One optimizer step of `micro` micro-batches (B, T) through the C ABI on
+    backend `be`, and the oracle's step on the same seeded inputs.  Returns
+    (mean micro loss, pre-clip norm, gradients, post-step parameters, oracle
+    result)."""
+    lc, oc, p = configs(p, B, T)
+    s = stream_for(p, B * T * micro + 1, data_seed)
+    batches = [inputs.batch_from_stream(s, B, T, k) for k in range(micro)]
+    say(f"case [{be.name}] layers={p['n_layer']} C={p['n_embd']} V={p['vocab_size']}/{p['padded_vocab']} "
+        f"B={B} T={T} micro={micro} {p['compute']}")
+    m = be.make(lc, seed)
+    losses = []
+    for x, y in batches:
+        losses.append(m.forward(be.dev(x), be.dev(y)))
+        m.backward(1.0 / micro)
+    names = m.param_names()
+    norm = m.step(lr, 1.0)
+    gg = gpu_grads(m, names)
+    pp = gpu_params(m, names)
+    m.close()
+    P = oracle_init(oc, seed)
+    ref = O.train_step(P, batches, oc, lr=lr, clip=1.0, t=1, dt=dt)
+    return float(np.mean(losses)), norm, gg, pp, ref
+
+
+def assert_fp32(loss, norm, gg, pp, ref, lr=6e-4):
+    """The fp32 path: loss and norm within 1e-4 relative, every gradient
+    within 1e-4 relative L2, post-AdamW parameters within 1e-3."""
+    say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
+    assert abs(loss - ref["loss"]) <= 1e-4 * abs(ref["loss"])
+    assert abs(norm - ref["norm"]) <= 1e-4 * ref["norm"]
+    for n in ref["grads"]:
+        assert rel_l2(gg[n], ref["grads"][n]) <= 1e-4, (n, rel_l2(gg[n], ref["grads"][n]))
+    check_post_adamw(pp, ref["params"], gg, ref["grads"], lr, exact=True)
+
+
+def assert_bf16(loss, norm, gg, pp, ref, lr=6e-4):
+    """The bf16 path: loss within 2e-2 relative, per-tensor gradient cosine
+    >= 0.999, the post-AdamW rule of check_post_adamw; the pre-clip norm
+    within 5e-2 relative is a looser extra check."""
+    say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
+    assert abs(loss - ref["loss"]) <= 2e-2 * abs(ref["loss"])
+    assert abs(norm - ref["norm"]) <= 5e-2 * ref["norm"]
+    worst = min((cosine(gg[n], ref["grads"][n]), n) for n in ref["grads"])
+    say("worst gradient cosine", worst)
+    assert worst[0] >= 0.999, worst
+    flips = check_post_adamw(pp, ref["params"], gg, ref["grads"], lr, exact=False)
+    say("sign-disagreement fraction", flips)
+    assert flips < 0.01

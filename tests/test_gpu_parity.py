@@ -1,233 +1,53 @@
 """GPU parity of the HIP training step (through the C ABI) against the CPU
-oracle on identical seeded inputs.
+oracle on identical seeded inputs, at small configurations that span several
+tiles and ragged tails.  The case bodies are in tests/parity_cases.py; the
+same cases run on the CPU emulation of the library in tests/test_emu_parity.py.
 
 Tolerances: the fp32 path within 1e-4 relative on the loss (and on every
 gradient, relative L2) and 1e-3 max-abs on the post-AdamW parameters; the
 bf16 path within 2e-2 relative on the loss, per-tensor gradient cosine
 >= 0.999, and the post-AdamW rule of check_post_adamw (1e-3 where the two
 gradients agree in sign)."""
-import numpy as np
 import pytest
 
-from decoder_only_transformer_02_amd import gpt2 as G
-from decoder_only_transformer_02_amd import inputs
-from oracle import gpt2_oracle as O
-from tests.gpu_helpers import (check_post_adamw, configs, cosine, gpu_grads, gpu_params,
-                               oracle_init, rel_l2, say, to_dev)
+from tests import parity_cases as cases
+from tests.gpu_helpers import GPU
 
 pytestmark = pytest.mark.gpu
 
-import torch  # noqa: E402
-
-SMALL_BF16 = dict(n_layer=2, n_head=2, n_embd=128, block_size=128, vocab_size=1000,
-                  padded_vocab=1000, compute="bf16", tokens="uniform")
-SMALL_FP32 = dict(n_layer=2, n_head=4, n_embd=64, block_size=64, vocab_size=301,
-                  padded_vocab=320, compute="fp32", tokens="uniform")
-
-
-def _stream(p, n, seed):
-    if p["tokens"] == "zipf":
-        return inputs.zipf_stream(seed, n, p["vocab_size"])
-    return inputs.uniform_stream(seed, n, p["vocab_size"])
-
-
-def run_step(p, B, T, seed=0, data_seed=1, lr=6e-4, dt=np.float64, micro=1):
-    lc, oc, p = configs(p, B, T)
-    s = _stream(p, B * T * micro + 1, data_seed)
-    batches = [inputs.batch_from_stream(s, B, T, k) for k in range(micro)]
-    say(f"case layers={p['n_layer']} C={p['n_embd']} V={p['vocab_size']}/{p['padded_vocab']} "
-        f"B={B} T={T} micro={micro} {p['compute']}")
-    m = G.GPT2Step(lc, seed=seed)
-    losses = []
-    for x, y in batches:
-        losses.append(m.forward(to_dev(x), to_dev(y)))
-        m.backward(1.0 / micro)
-    names = m.param_names()
-    norm = m.step(lr, 1.0)
-    gg = gpu_grads(m, names)
-    pp = gpu_params(m, names)
-    m.close()
-    P = oracle_init(oc, seed)
-    ref = O.train_step(P, batches, oc, lr=lr, clip=1.0, t=1, dt=dt)
-    return float(np.mean(losses)), norm, gg, pp, ref
-
-
-def assert_fp32(loss, norm, gg, pp, ref, lr=6e-4):
-    say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
-    assert abs(loss - ref["loss"]) <= 1e-4 * abs(ref["loss"])
-    assert abs(norm - ref["norm"]) <= 1e-4 * ref["norm"]
-    for n in ref["grads"]:
-        assert rel_l2(gg[n], ref["grads"][n]) <= 1e-4, (n, rel_l2(gg[n], ref["grads"][n]))
-    check_post_adamw(pp, ref["params"], gg, ref["grads"], lr, exact=True)
-
-
-def assert_bf16(loss, norm, gg, pp, ref, lr=6e-4):
-    say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
-    assert abs(loss - ref["loss"]) <= 2e-2 * abs(ref["loss"])
-    assert abs(norm - ref["norm"]) <= 5e-2 * ref["norm"]
-    worst = min((cosine(gg[n], ref["grads"][n]), n) for n in ref["grads"])
-    say("worst gradient cosine", worst)
-    assert worst[0] >= 0.999, worst
-    flips = check_post_adamw(pp, ref["params"], gg, ref["grads"], lr, exact=False)
-    say("sign-disagreement fraction", flips)
-    assert flips < 0.01
-
-
-# ---------------------------------------------------------------------------- fp32 path
 
 def test_tiny_fp32_step():
-    """Tiny GPT-2-shaped decoder, fp32 throughout, B=4 T=64, seed 0."""
-    p = inputs.PRESETS["tiny"]
-    assert_fp32(*run_step(p, 4, 64, seed=0, data_seed=0))
+    cases.tiny_fp32_step(GPU)
 
 
 def test_fp32_ragged_shapes():
-    """Ragged M, T, vocabulary tiles; generic attention kernels."""
-    assert_fp32(*run_step(SMALL_FP32, 3, 37, seed=3, data_seed=5))
+    cases.fp32_ragged_shapes(GPU)
 
-
-# ---------------------------------------------------------------------------- bf16 path
 
 def test_bf16_ragged_mfma_paths():
-    """head_dim 64 (matrix-core attention), T=100 (ragged key / query
-    tiles), M=300 (ragged GEMM rows), vocabulary 1000 (ragged classifier
-    tiles and unaligned cross-entropy rows)."""
-    assert_bf16(*run_step(SMALL_BF16, 3, 100, seed=1, data_seed=2))
+    cases.bf16_ragged_mfma_paths(GPU)
 
 
 def test_bf16_accumulation_matches_one_big_batch():
-    """4 micro-steps at loss scale 1/4 equal one batch 4x as large."""
-    lc, oc, p = configs(SMALL_BF16, 8, 64)
-    s = _stream(p, 8 * 64 + 1, 9)
-    x, y = inputs.batch_from_stream(s, 8, 64)
-    m = G.GPT2Step(lc, seed=0)
-    m.forward(to_dev(x), to_dev(y))
-    m.backward(1.0)
-    names = m.param_names()
-    g1 = gpu_grads(m, names)
-    m.zero_grad()
-    for k in range(4):
-        m.forward(to_dev(x[2 * k:2 * k + 2]), to_dev(y[2 * k:2 * k + 2]))
-        m.backward(0.25)
-    g4 = gpu_grads(m, names)
-    m.close()
-    for n in names:
-        assert cosine(g1[n], g4[n]) >= 0.9999, n
+    cases.bf16_accumulation_matches_one_big_batch(GPU)
 
-
-# ---------------------------------------------------------------------------- invariants
 
 @pytest.mark.parametrize("preset", ["fp32", "bf16"])
 def test_causality_bitwise(preset):
-    p = SMALL_FP32 if preset == "fp32" else SMALL_BF16
-    B, T = 2, 64
-    lc, oc, p = configs(p, B, T)
-    m = G.GPT2Step(lc, seed=0)
-    x, _ = inputs.batch_from_stream(_stream(p, B * T + 1, 4), B, T)
-    t = 40
-    m.forward(to_dev(x))
-    Vp = p["padded_vocab"]
-    z0 = m.view("logits")[:B * T, :Vp].clone().view(B, T, -1)
-    x2 = x.copy()
-    x2[:, t + 1] = (x2[:, t + 1] + 11) % p["vocab_size"]
-    m.forward(to_dev(x2))
-    z1 = m.view("logits")[:B * T, :Vp].clone().view(B, T, -1)
-    m.close()
-    assert torch.equal(z0[:, :t + 1], z1[:, :t + 1])
-    assert not torch.equal(z0[:, t + 1], z1[:, t + 1])
+    cases.causality_bitwise(GPU, preset)
 
 
 def test_determinism_bitwise():
-    p = SMALL_BF16
-    outs = []
-    for _ in range(2):
-        lc, oc, pp = configs(p, 3, 100)
-        x, y = inputs.batch_from_stream(_stream(pp, 301, 7), 3, 100)
-        m = G.GPT2Step(lc, seed=0)
-        loss = m.forward(to_dev(x), to_dev(y))
-        m.backward(1.0)
-        norm = m.step(6e-4)
-        names = m.param_names()
-        outs.append((loss, norm, gpu_grads(m, names), gpu_params(m, names)))
-        m.close()
-    assert outs[0][0] == outs[1][0] and outs[0][1] == outs[1][1]
-    for n in outs[0][2]:
-        assert np.array_equal(outs[0][2][n], outs[1][2][n]), n
-        assert np.array_equal(outs[0][3][n], outs[1][3][n]), n
+    cases.determinism_bitwise(GPU)
 
 
 def test_device_init_equals_host_init():
-    lc, oc, p = configs(SMALL_BF16, 2, 16)
-    m = G.GPT2Step(lc, seed=5)
-    flat = np.concatenate([m.view(n).cpu().numpy().ravel() for n in m.param_names()])
-    m.close()
-    host = G.init_host(lc, 5)
-    assert np.array_equal(flat, host)
-    ref = np.concatenate([v.ravel() for v in O.init_params(oc, 5).values()])
-    assert np.all(np.abs(flat - ref) <= np.spacing(np.abs(ref)))
+    cases.device_init_equals_host_init(GPU)
 
 
 def test_error_paths():
-    lc, oc, p = configs(SMALL_FP32, 2, 16)
-    m = G.GPT2Step(lc, seed=0)
-    x, y = inputs.batch_from_stream(_stream(p, 33, 1), 2, 16)
-    with pytest.raises(G.GPT2Error) as e:
-        m.backward(1.0)
-    assert e.value.status == G.GPT2_E_STATE
-    with pytest.raises(G.GPT2Error) as e:
-        m.step(1e-3)
-    assert e.value.status == G.GPT2_E_STATE
-    with pytest.raises(G.GPT2Error) as e:
-        m.forward(to_dev(np.zeros((3, 16), np.int32)), to_dev(np.zeros((3, 16), np.int32)))
-    assert e.value.status == G.GPT2_E_SHAPE
-    bad = x.copy()
-    bad[1, 3] = p["vocab_size"]
-    with pytest.raises(G.GPT2Error) as e:
-        m.forward(to_dev(bad), to_dev(y))
-    assert e.value.status == G.GPT2_E_TOKEN
-    badt = y.copy()
-    badt[0, 0] = -1
-    with pytest.raises(G.GPT2Error) as e:
-        m.forward(to_dev(x), to_dev(badt))
-    assert e.value.status == G.GPT2_E_TOKEN
-    # a NaN planted in a weight: the norm is not finite, the update is skipped
-    m.forward(to_dev(x), to_dev(y))
-    m.backward(1.0)
-    before = {n: m.view(n).clone() for n in m.param_names()}
-    m.view("grad.h0.fc.w")[0, 0] = float("nan")
-    with pytest.raises(G.GPT2Error) as e:
-        m.step(1e-3)
-    assert e.value.status == G.GPT2_E_NONFINITE
-    for n in before:
-        assert torch.equal(before[n], m.view(n)), n
-    # still usable afterwards
-    loss = m.forward(to_dev(x), to_dev(y))
-    m.backward(1.0)
-    assert np.isfinite(m.step(1e-3)) and np.isfinite(loss)
-    m.close()
+    cases.error_paths(GPU)
 
 
 def test_overfit_single_batch_tracks_oracle():
-    """The chapter "optimization loop: overfit a single batch": repeated steps
-    on one tiny fp32 batch; the loss curve follows the oracle's."""
-    p = inputs.PRESETS["tiny"]
-    lc, oc, p = configs(p, 4, 64)
-    x, y = inputs.batch_from_stream(_stream(p, 257, 0), 4, 64)
-    m = G.GPT2Step(lc, seed=0)
-    gl = []
-    for _ in range(25):
-        gl.append(m.forward(to_dev(x), to_dev(y)))
-        m.backward(1.0)
-        m.step(1e-3)
-    m.close()
-    P = oracle_init(oc, 0)
-    Ms = Vs = None
-    ol = []
-    for t in range(1, 6):
-        r = O.train_step(P, [(x, y)], oc, lr=1e-3, clip=1.0, t=t, M_state=Ms, V_state=Vs)
-        ol.append(r["loss"])
-        P, Ms, Vs = r["params"], r["m"], r["v"]
-    say("gpu", gl[:5], "oracle", ol)
-    for a, b in zip(gl[:5], ol):
-        assert abs(a - b) <= 1e-4 * abs(b)
-    assert gl[-1] < gl[0] - 1.0
+    cases.overfit_single_batch_tracks_oracle(GPU)
