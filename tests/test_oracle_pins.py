@@ -308,6 +308,40 @@ def test_accumulation_is_linear():
         np.testing.assert_allclose(G_sum[n], G_full[n], rtol=1e-11, atol=1e-17, err_msg=n)
 
 
+def test_train_step_micro_batches_equal_one_batch():
+    """train_step over k micro-batches of B sequences (loss scale 1/k, summed
+    gradients, the loss reported as the mean of the micro losses) equals the
+    same whole step on one batch of k*B sequences: loss, gradients, norm,
+    clip coefficient, new parameters and both AdamW moments ("Scaling
+    Training with Gradient Accumulation & DDP": the loss is divided by the
+    number of accumulation steps).  A wrong 1/k, a loss averaged with the
+    wrong weight or a gradient summed twice fails it.  The clip threshold is
+    set below the norm so the coefficient is active."""
+    cfg = TINY
+    P = O.init_params(cfg, 0)
+    s = inputs.uniform_stream(5, 6 * 16 + 1, 512)
+    xb, yb = inputs.batch_from_stream(s, 6, 16)
+    whole = O.train_step(P, [(xb, yb)], cfg, lr=1e-3, clip=0.5, t=1)
+    for k in (2, 3, 6):
+        b = 6 // k
+        micro = [(xb[i * b:(i + 1) * b], yb[i * b:(i + 1) * b]) for i in range(k)]
+        r = O.train_step(P, micro, cfg, lr=1e-3, clip=0.5, t=1)
+        assert r["loss"] == pytest.approx(whole["loss"], rel=1e-13), k
+        assert r["norm"] == pytest.approx(whole["norm"], rel=1e-12), k
+        assert whole["coef"] < 1.0 and r["coef"] == pytest.approx(whole["coef"], rel=1e-12), k
+        for n in whole["grads"]:
+            np.testing.assert_allclose(r["grads"][n], whole["grads"][n], rtol=1e-10, atol=1e-16,
+                                       err_msg=f"{k} {n}")
+            np.testing.assert_allclose(r["params"][n], whole["params"][n], rtol=0, atol=1e-7,
+                                       err_msg=f"{k} {n}")
+            np.testing.assert_allclose(r["m"][n], whole["m"][n], rtol=1e-10, atol=1e-17, err_msg=n)
+            np.testing.assert_allclose(r["v"][n], whole["v"][n], rtol=1e-9, atol=1e-24, err_msg=n)
+    # one micro-batch's loss alone differs from the whole batch's mean, so
+    # the averaging is really exercised
+    first = O.train_step(P, [(xb[:1], yb[:1])], cfg, lr=1e-3, clip=0.5, t=1)
+    assert abs(first["loss"] - whole["loss"]) > 1e-4
+
+
 def test_clip_gives_min_norm_one():
     rng = np.random.default_rng(0)
     for scale in (0.01, 10.0):
