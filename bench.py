@@ -1,10 +1,23 @@
 """Throughput of one GPT-2 124M training step (forward, backward, global-norm
 clip, AdamW) at B=16, T=1024, bf16, on one MI355X, through the C ABI.
 
-Prints one JSON line: tokens/s (whole job), ms/step, MFU, the roofline of
-the dominant kernel (the classifier GEMM, timed live with HIP events on the
-library stream over the timed region), and the CPU oracle timed on a
-bounded sample of the same workload on this host."""
+Prints one JSON line:
+  * value: tokens/s of the whole job (wall clock over exactly `--steps`
+    steps between two device synchronizations), ms/step (mean), and the
+    median / p10 / p90 of per-step HIP-event times on the library stream;
+  * mfu: (6N + 6 L C (T+1)) flops per token against the bf16 dense peak;
+  * roofline: the dominant kernel (the classifier forward GEMM), its
+    algorithmic flops over its HIP-event launch time;
+  * kernels: every timing class of the library with its algorithmic work
+    per step (the scope table's per-unit figures times the units of one
+    step), its time per step and its fraction of the MI355X roofline;
+  * padding: the classifier GEMMs + cross-entropy and the whole step at the
+    unpadded vocabulary 50257 against the padded 50304;
+  * accumulated_step: one optimizer step of 32 micro-steps of B=32, T=512
+    (524,288 tokens) with clip and AdamW at lr(132);
+  * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+Inputs are resident in device memory before every timed region.
+"""
 import argparse
 import json
 import os
@@ -15,7 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
-PEAK_HBM = 8.0e12      # bytes/s
+PEAK_HBM = 8.0e12      # MI355X HBM3E, bytes/s
+METRIC = "train tokens/sec + ms/step, GPT-2 124M B=16 T=1024 bf16; MFU vs peak"
 
 
 def flops_per_token(L, C, T, n_nonemb):
@@ -23,10 +37,69 @@ def flops_per_token(L, C, T, n_nonemb):
     return 6 * n_nonemb + 6 * L * C * (T + 1)
 
 
-def cpu_baseline(preset, seconds_hint=True):
+def percentile(xs, q):
+    """Linear-interpolation percentile (q in [0, 100]) of a non-empty list."""
+    s = sorted(xs)
+    if len(s) == 1:
+        return s[0]
+    pos = (len(s) - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
+
+
+def class_work(p, B, T, n_params):
+    """Algorithmic work of one training step per timing class: (bound, amount,
+    unit) with flops for matrix-core classes and bytes for bandwidth classes.
+
+    GEMMs: 2 M K N per product; per layer the four weight products
+    (3C, C, 4C, 4C outputs of widths C, C, C, 4C) three times (forward, dX,
+    dW), plus the classifier (M x Vp x C) three times.  Attention: 4 hd flops
+    per causal score (QK^T and PV) forward, twice that backward (recompute
+    not credited).  LayerNorm forward (6C+8) and backward (14C+8) bytes per
+    token over 2L+1 LayerNorms; cross-entropy (4 Vp + 8) bytes per token;
+    gradient norm 4 bytes and AdamW 30 bytes per parameter."""
+    L, C, H, Vp = p["n_layer"], p["n_embd"], p["n_head"], p["padded_vocab"]
+    M = B * T
+    hd = C // H
+    gemm = 3 * 2 * M * (L * 12 * C * C + Vp * C)
+    lm = 2 * M * Vp * C
+    attn = L * B * H * (T * (T + 1) // 2) * hd * 4
+    return {
+        "lmhead_fwd": ("mfma", lm, "flop"),
+        "gemm": ("mfma", gemm, "flop"),
+        "attn_fwd": ("mfma", attn, "flop"),
+        "attn_bwd": ("mfma", 2 * attn, "flop"),
+        "ln_fwd": ("hbm", (2 * L + 1) * M * (6 * C + 8), "byte"),
+        "ln_bwd": ("hbm", (2 * L + 1) * M * (14 * C + 8), "byte"),
+        "xent": ("hbm", M * (4 * Vp + 8), "byte"),
+        "norm": ("hbm", 4 * n_params, "byte"),
+        "adamw": ("hbm", 30 * n_params, "byte"),
+    }
+
+
+def roofline_entry(bound, work, ms):
+    """Achieved rate and fraction of the MI355X peak for `work` done in `ms`."""
+    if bound == "mfma":
+        ach = work / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": round(ach * 1e12 / PEAK_BF16, 4)}
+    ach = work / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(ach * 1e9 / PEAK_HBM, 4)}
+
+
+def cpu_baseline(preset):
+    """The oracle as it stands, one full step on one sequence of T tokens of
+    the same model (a bounded sample of the benchmark batch)."""
     import numpy as np
     from decoder_only_transformer_02_amd import inputs
     from oracle import gpt2_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = None
     oc = O.Config(preset["n_layer"], preset["n_head"], preset["n_embd"], preset["block_size"],
                   preset["vocab_size"], preset["padded_vocab"])
     P = O.init_params(oc, 0)
@@ -35,11 +108,71 @@ def cpu_baseline(preset, seconds_hint=True):
     t0 = time.perf_counter()
     O.train_step(P, [(x, y)], oc, lr=6e-4, clip=1.0, t=1, dt=np.float32)
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step (forward, backward, clip, AdamW) of the same model on one "
-                      f"sequence of {T} tokens, float32 storage with float64 reductions, "
-                      f"{dt:.1f} s"}
+    cores = blas_threads or len(os.sched_getaffinity(0))
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full step (forward, backward, clip, AdamW) of the same model on one sequence "
+                      f"of {T} tokens (1/{preset['B']} of the benchmark batch), float32 storage with "
+                      f"float64 reductions, {dt:.1f} s; host has {os.cpu_count()} CPUs, "
+                      f"{len(os.sched_getaffinity(0))} in this process's affinity, BLAS threads "
+                      f"{blas_threads}"}
+
+
+class Runner:
+    """One library context with device-resident inputs of a preset."""
+
+    def __init__(self, G, inputs, torch, preset, micro=1):
+        self.torch = torch
+        self.p = preset
+        self.B, self.T = preset["B"], preset["T"]
+        cfg = G.make_config(**{**preset, "max_batch": self.B, "max_seq": self.T})
+        self.cfg = cfg
+        self.m = G.GPT2Step(cfg, seed=0)
+        n = self.B * self.T
+        s = inputs.zipf_stream(0, n * micro + 1, preset["vocab_size"])
+        self.batches = []
+        for k in range(micro):
+            x, y = inputs.batch_from_stream(s, self.B, self.T, k)
+            self.batches.append((torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()))
+        torch.cuda.synchronize()
+
+    def step(self, lr=6e-4):
+        k = len(self.batches)
+        for x, y in self.batches:
+            self.m.forward(x, y, sync=False)
+            self.m.backward(1.0 / k)
+        self.m.step(lr, 1.0, sync=False)
+
+    def timed(self, steps, warmup, lr=6e-4):
+        """Wall-clock seconds of exactly `steps` steps between two device
+        synchronizations, and the per-step HIP-event times (ms)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(lr)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record()
+            self.step(lr)
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, [a.elapsed_time(b) for a, b in ev]
+
+    def class_ms(self, cls, steps=3):
+        """Milliseconds per step and brackets per step of one timing class."""
+        self.m.timing_enable(cls)
+        for _ in range(steps):
+            self.step()
+        ms, n = self.m.timing_read()
+        self.m.timing_enable("none")
+        return ms / steps, n / steps
+
+    def close(self):
+        self.m.close()
+        self.torch.cuda.synchronize()
 
 
 def main():
@@ -48,83 +181,108 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--preset", default="gpt2_124m")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the unpadded-vocabulary and accumulated-step measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the data-parallel exchange is not built)", file=sys.stderr)
         sys.exit(2)
 
+    import ctypes
     import torch
     from decoder_only_transformer_02_amd import gpt2 as G
     from decoder_only_transformer_02_amd import inputs
 
-    p = inputs.PRESETS[args.preset]
+    p = inputs.PRESETS["gpt2_124m"]
     B, T = p["B"], p["T"]
-    cfg = G.make_config(**{**p, "max_batch": B, "max_seq": T})
-    m = G.GPT2Step(cfg, seed=0)
-    x, y = inputs.batch_from_stream(inputs.zipf_stream(0, B * T + 1, p["vocab_size"]), B, T)
-    xd = torch.from_numpy(x).cuda()
-    yd = torch.from_numpy(y).cuda()
-    lr = 6e-4
-
-    def step():
-        m.forward(xd, yd, sync=False)
-        m.backward(1.0)
-        m.step(lr, 1.0, sync=False)
-
-    print(f"warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    m.timing_enable("lmhead_fwd")
-    print(f"timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    k_ms, k_n = m.timing_read()
-    m.timing_enable("none")
-    loss = m.forward(xd, yd, sync=True)
-
-    ms = dt / args.steps * 1e3
-    tokens = B * T * args.steps / dt
-    n_total = G.lib().gpt2_num_params(__import__("ctypes").byref(cfg))
+    print(f"config 124M B={B} T={T}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    r = Runner(G, inputs, torch, p)
+    wall, ev_ms = r.timed(args.steps, args.warmup)
+    ms = wall / args.steps * 1e3
+    tokens = B * T * args.steps / wall
+    n_total = G.lib().gpt2_num_params(ctypes.byref(r.cfg))
     n_mfu = n_total - p["block_size"] * p["n_embd"] - (p["padded_vocab"] - p["vocab_size"]) * p["n_embd"]
     fpt = flops_per_token(p["n_layer"], p["n_embd"], T, n_mfu)
-    mfu = tokens * fpt / PEAK_BF16
-    avg_k = k_ms / max(k_n, 1) * 1e-3
-    k_flops = 2.0 * B * T * p["padded_vocab"] * p["n_embd"]
-    achieved = k_flops / avg_k / 1e12
+    work = class_work(p, B, T, n_total)
+
+    print("per-class kernel timing", file=sys.stderr, flush=True)
+    kernels = {}
+    for cls in ("lmhead_fwd", "gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "xent", "norm", "adamw",
+                "transpose", "embed", "colsum"):
+        c_ms, c_n = r.class_ms(cls)
+        k = {"ms_per_step": round(c_ms, 4), "launches_per_step": c_n}
+        if cls in work:
+            bound, amount, unit = work[cls]
+            k.update({"work_per_step": amount, "work_unit": unit})
+            k.update(roofline_entry(bound, amount, c_ms))
+        kernels[cls] = k
+    loss = r.m.forward(*r.batches[0], sync=True)
+    r.close()
+    del r
+
+    lm = kernels["lmhead_fwd"]
     out = {
-        "metric": "train tokens/sec + ms/step, GPT-2 124M B=16 T=1024 bf16; MFU vs peak",
+        "metric": METRIC,
         "value": round(tokens, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(percentile(ev_ms, 50), 3),
+        "ms_per_step_p10": round(percentile(ev_ms, 10), 3),
+        "ms_per_step_p90": round(percentile(ev_ms, 90), 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.preset}: GPT-2 124M train step, B={B}, T={T}, vocab "
-                               f"{p['vocab_size']} padded to {p['padded_vocab']}, Zipf(1.1) ids",
+        "config": {"workload": f"GPT-2 124M train step (forward, backward, clip, AdamW), B={B}, T={T}, "
+                               f"vocabulary {p['vocab_size']} padded to {p['padded_vocab']}, Zipf(1.1) ids",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "mfu": round(mfu, 4),
+        "mfu": round(tokens * fpt / PEAK_BF16, 4),
         "flops_per_token": fpt,
         "loss": round(loss, 5),
-        "roofline": {"kernel": "classifier GEMM forward (k_gemm_nt, EPI_LOGITS)",
-                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16 / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
-                     "traffic": None, "avg_launch_ms": round(avg_k * 1e3, 4),
-                     "launches": k_n},
+        "roofline": {"kernel": "classifier GEMM forward (k_gemm_nt 256x256, EPI_LOGITS)",
+                     "bound": "mfma", "achieved": lm["achieved"], "peak": lm["peak"], "unit": "TFLOP/s",
+                     "frac": lm["frac"], "traffic": None,
+                     "avg_launch_ms": round(lm["ms_per_step"] / max(lm["launches_per_step"], 1), 4),
+                     "launches": lm["launches_per_step"]},
+        "kernels": kernels,
     }
-    del m
-    torch.cuda.synchronize()
+
+    if not args.no_extra:
+        print("unpadded vocabulary", file=sys.stderr, flush=True)
+        u = Runner(G, inputs, torch, inputs.PRESETS["gpt2_124m_v50257"])
+        u_wall, u_ev = u.timed(max(5, args.steps // 2), 2)
+        u_lm, _ = u.class_ms("lmhead_fwd")
+        u_gemm_x = u.class_ms("xent")[0]
+        u.close()
+        del u
+        pad_ms = kernels["lmhead_fwd"]["ms_per_step"] + kernels["xent"]["ms_per_step"]
+        unpad_ms = u_lm + u_gemm_x
+        out["padding"] = {
+            "classifier_fwd_plus_xent_ms": {"vocab_50304": round(pad_ms, 4), "vocab_50257": round(unpad_ms, 4)},
+            "step_ms_median": {"vocab_50304": round(percentile(ev_ms, 50), 3),
+                               "vocab_50257": round(percentile(u_ev, 50), 3)},
+            "step_speedup_from_padding": round(percentile(u_ev, 50) / percentile(ev_ms, 50) - 1.0, 4),
+        }
+        print("accumulated step (32 x B=32 T=512)", file=sys.stderr, flush=True)
+        pa = inputs.PRESETS["gpt2_124m_accum"]
+        a = Runner(G, inputs, torch, pa, micro=pa["accum"])
+        a_wall, a_ev = a.timed(3, 1, lr=G.lr_at(pa["lr_step"]))
+        a.close()
+        del a
+        a_tok = pa["B"] * pa["T"] * pa["accum"]
+        a_ms = percentile(a_ev, 50)
+        out["accumulated_step"] = {
+            "tokens_per_step": a_tok, "ms_per_step_median": round(a_ms, 2),
+            "ms_per_step_wall_mean": round(a_wall / 3 * 1e3, 2),
+            "tokens_per_s": round(a_tok / (a_ms * 1e-3), 1),
+            "mfu": round(a_tok / (a_ms * 1e-3) * flops_per_token(pa["n_layer"], pa["n_embd"], pa["T"], n_mfu)
+                         / PEAK_BF16, 4)}
     if not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p)

@@ -462,6 +462,11 @@ hipError_t ln_backward(gpt2_ctx* c, int k, int wj, const void* dy, bool accum, f
                                   beta, c->st);
 }
 
+hipError_t colsum_timed(gpt2_ctx* c, const void* X, int M, int N, int ldx, float* db, float beta) {
+  Timed t(c, GPT2_T_COLSUM);
+  return gk::colsum(X, c->bf, M, N, ldx, db, beta, c->col_part, c->st);
+}
+
 // dX[M, in] = dY[M, out] W[out, in]: NT against the transposed copy in bf16,
 // NN (B transposed in memory) in fp32.
 GemmArgs dx_args(gpt2_ctx* c, int M, int n_in, int n_out, const void* dY, int ldy, int wj, int kind,
@@ -483,7 +488,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
                 c->G(c->li(l, 10)), 4 * C);
   g.beta = beta;
   KCHK(run_gemm(c, g));
-  KCHK(gk::colsum(c->dres_act, c->bf, M, C, C, c->G(c->li(l, 11)), beta, c->col_part, c->st));
+  KCHK(colsum_timed(c, c->dres_act, M, C, C, c->G(c->li(l, 11)), beta));
   // fc: da2 = du W_fc; dW_fc = du^T a2; db_fc = sum du
   g = dx_args(c, M, C, 4 * C, c->du, 4 * C, c->li(l, 8), gk::EPI_STORE, c->dA, C);
   KCHK(run_gemm(c, g));
@@ -491,7 +496,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
                 c->G(c->li(l, 8)), C);
   g.beta = beta;
   KCHK(run_gemm(c, g));
-  KCHK(gk::colsum(c->du, c->bf, M, 4 * C, 4 * C, c->G(c->li(l, 9)), beta, c->col_part, c->st));
+  KCHK(colsum_timed(c, c->du, M, 4 * C, 4 * C, c->G(c->li(l, 9)), beta));
   KCHK(ln_backward(c, 2 * l + 1, c->li(l, 6), c->dA, true, beta, M));
   // attention projection: do = dr W_proj; dW_proj = dr^T o; db_proj
   g = dx_args(c, M, C, C, c->dres_act, C, c->li(l, 4), gk::EPI_STORE, c->dattn, C);
@@ -500,7 +505,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
                 c->G(c->li(l, 4)), C);
   g.beta = beta;
   KCHK(run_gemm(c, g));
-  KCHK(gk::colsum(c->dres_act, c->bf, M, C, C, c->G(c->li(l, 5)), beta, c->col_part, c->st));
+  KCHK(colsum_timed(c, c->dres_act, M, C, C, c->G(c->li(l, 5)), beta));
   {
     Timed t(c, GPT2_T_ATTN_BWD);
     KCHK(gk::attn_bwd(c->qkv[l], c->att[l], c->dattn, c->lse[l], c->dqkv, c->attn_ws, B, T, c->H,
@@ -513,7 +518,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
                 c->G(c->li(l, 2)), C);
   g.beta = beta;
   KCHK(run_gemm(c, g));
-  KCHK(gk::colsum(c->dqkv, c->bf, M, 3 * C, 3 * C, c->G(c->li(l, 3)), beta, c->col_part, c->st));
+  KCHK(colsum_timed(c, c->dqkv, M, 3 * C, 3 * C, c->G(c->li(l, 3)), beta));
   KCHK(ln_backward(c, 2 * l, c->li(l, 0), c->dA, true, beta, M));
   return hipSuccess;
 }
@@ -521,6 +526,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
 // Refreshes the transposed bf16 copies from the bf16 weight copies.
 hipError_t refresh_transposed(gpt2_ctx* c) {
   if (!c->bf) return hipSuccess;
+  Timed t(c, GPT2_T_TRANSPOSE);
   for (size_t j = 0; j < c->specs.size(); ++j) {
     if (c->toff[j] == (size_t)-1) continue;
     const auto& sp = c->specs[j];
@@ -710,7 +716,10 @@ GPT2_API gpt2_status gpt2_forward(gpt2_ctx* c, const int32_t* d_tokens, const in
   c->T = T;
   HIPCHK(c, hipMemsetAsync(c->flag, 0, 16, c->st));
   HIPCHK(c, hipMemcpyAsync(c->tok, d_tokens, (size_t)M * 4, hipMemcpyDeviceToDevice, c->st));
-  HIPCHK(c, gk::embed_fwd(c->tok, c->P(0), c->P(1), c->h[0], M, T, C, c->V, c->flag, c->st));
+  {
+    Timed t(c, GPT2_T_EMBED);
+    HIPCHK(c, gk::embed_fwd(c->tok, c->P(0), c->P(1), c->h[0], M, T, C, c->V, c->flag, c->st));
+  }
   for (int l = 0; l < c->L; ++l) HIPCHK(c, fwd_layer(c, l, M, B, T));
   const int lf = 2 + 12 * c->L;
   {
@@ -762,8 +771,11 @@ GPT2_API gpt2_status gpt2_backward(gpt2_ctx* c, float grad_scale) {
   const int lf = 2 + 12 * L;
   HIPCHK(c, ln_backward(c, 2 * L, lf, c->dA, false, beta, M));
   for (int l = L - 1; l >= 0; --l) HIPCHK(c, bwd_layer(c, l, M, B, T, beta));
-  HIPCHK(c, gk::embed_bwd(c->tok, c->dres, c->G(0), c->G(1), B, T, C, c->V, c->cfg.block_size, beta,
-                          c->emb_ws, c->st));
+  {
+    Timed t(c, GPT2_T_EMBED);
+    HIPCHK(c, gk::embed_bwd(c->tok, c->dres, c->G(0), c->G(1), B, T, C, c->V, c->cfg.block_size, beta,
+                            c->emb_ws, c->st));
+  }
   c->armed_bwd = false;
   c->armed_step = true;
   c->grads_fresh = false;
@@ -793,8 +805,8 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
     Timed t(c, GPT2_T_ADAMW);
     HIPCHK(c, gk::adamw(c->params, c->grads, c->am, c->av, c->shadow, c->chunks, c->nchunks, c->scal,
                         lr, c->cfg.beta1, c->cfg.beta2, c->cfg.adam_eps, c->cfg.weight_decay, c->st));
-    HIPCHK(c, refresh_transposed(c));
   }
+  HIPCHK(c, refresh_transposed(c));
   c->armed_step = false;
   c->grads_fresh = true;
   if (h_grad_norm) {
@@ -858,7 +870,7 @@ GPT2_API gpt2_status gpt2_tensor_info(const gpt2_ctx* c, int32_t i, gpt2_tensor_
 GPT2_API gpt2_status gpt2_timing_enable(gpt2_ctx* c, int32_t kernel_class) {
   gpt2_status s = check_ctx(c);
   if (s) return s;
-  if (kernel_class < 0 || kernel_class > GPT2_T_NORM) return fail(c, GPT2_E_ARG, "bad kernel class");
+  if (kernel_class < 0 || kernel_class > GPT2_T_COLSUM) return fail(c, GPT2_E_ARG, "bad kernel class");
   c->tclass = kernel_class;
   c->ev_used = 0;
   return GPT2_OK;

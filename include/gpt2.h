@@ -185,11 +185,19 @@ gpt2_status gpt2_tensor_info(const gpt2_ctx* c, int32_t i, gpt2_tensor_desc* out
 
 /* Kernel timing with HIP events on the library stream.  kernel_class
  * selects which launches are bracketed (GPT2_T_*); 0 turns timing off.
- * gpt2_timing_read synchronizes, returns the summed milliseconds and the
- * launch count since the last read, and resets them. */
+ * One bracket covers one library operation of that class (a GEMM with its
+ * split-K reduction, a LayerNorm backward with its parameter-gradient
+ * reduction, ...).  Classes: the classifier forward GEMM alone; every GEMM
+ * (the classifier forward included); attention forward; attention backward;
+ * LayerNorm forward; LayerNorm backward; cross-entropy; AdamW; gradient
+ * norm; refresh of the transposed bf16 weight copies; embedding forward and
+ * backward; bias-gradient column sums.  gpt2_timing_read synchronizes,
+ * returns the summed milliseconds and the bracket count since the last
+ * read, and resets them. */
 enum { GPT2_T_NONE = 0, GPT2_T_LMHEAD_FWD = 1, GPT2_T_GEMM = 2, GPT2_T_ATTN_FWD = 3,
        GPT2_T_ATTN_BWD = 4, GPT2_T_LN_FWD = 5, GPT2_T_LN_BWD = 6, GPT2_T_XENT = 7,
-       GPT2_T_ADAMW = 8, GPT2_T_NORM = 9 };
+       GPT2_T_ADAMW = 8, GPT2_T_NORM = 9, GPT2_T_TRANSPOSE = 10, GPT2_T_EMBED = 11,
+       GPT2_T_COLSUM = 12 };
 gpt2_status gpt2_timing_enable(gpt2_ctx* c, int32_t kernel_class);
 gpt2_status gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches);
 
