@@ -27,6 +27,7 @@ def emu_lib():
         sig = {
             "emu_set_range_mode": (None, [I]),
             "emu_set_reverse_order": (None, [I]),
+            "emu_set_land_early": (None, [I]),
             "emu_collectives": (ct.c_long, []),
             "emu_gemm": (I, [I, I, I, P, I, I, P, I, I, I, P, I, P, P, P, F, F, I, P, SZ]),
             "emu_gemm_splitk_ws_elems": (SZ, [I, I, I]),

@@ -71,6 +71,7 @@ struct Worker {
 thread_local Worker* W = nullptr;
 int g_range_mode = 0;      // 0: scalar offset counted by the range check; 1: not counted
 int g_reverse_order = 0;   // schedule lanes and waves in reverse order
+int g_land_early = 0;      // buffer-to-LDS writes land at issue instead of at the covering wait
 std::atomic<long> g_collectives{0};
 
 [[noreturn]] void fatal(const std::string& m) {
@@ -420,6 +421,12 @@ void buf_fn(void*) {
     }
     grp.push_back(pw);
   }
+  if (g_land_early) {
+    // the earliest the hardware may write LDS: right at issue.  The group
+    // still counts for vmcnt, so the waits keep their meaning.
+    for (auto& pw : grp) std::memcpy(pw.dst, pw.data, pw.n);
+    for (auto& pw : grp) pw.n = 0;
+  }
   w.q.push_back(std::move(grp));
 }
 }  // namespace
@@ -487,6 +494,7 @@ extern "C" void emu_fiber_main() {
 // ------------------------------------------------------------------ emulator controls
 extern "C" __attribute__((visibility("default"))) void emu_set_range_mode(int m) { emu::g_range_mode = m; }
 extern "C" __attribute__((visibility("default"))) void emu_set_reverse_order(int r) { emu::g_reverse_order = r; }
+extern "C" __attribute__((visibility("default"))) void emu_set_land_early(int e) { emu::g_land_early = e; }
 extern "C" __attribute__((visibility("default"))) long emu_collectives() { return emu::g_collectives.load(); }
 
 // ------------------------------------------------------------------ runtime API

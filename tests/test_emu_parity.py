@@ -25,6 +25,7 @@ def emu_mode():
     yield L
     L.emu_set_range_mode(0)
     L.emu_set_reverse_order(0)
+    L.emu_set_land_early(0)
 
 
 def test_emu_tiny_fp32_step():
@@ -59,15 +60,20 @@ def test_emu_bf16_ragged_mfma_paths(emu_mode, range_mode):
 
 def test_emu_results_independent_of_range_mode_and_schedule(emu_mode):
     """Bitwise the same step with the range check including the scalar
-    offset or not, and with the fibers of every block scheduled in reverse
-    order (an LDS race or a missing wait would show as a difference)."""
+    offset or not, with the fibers of every block scheduled in reverse
+    order, and with buffer-to-LDS writes landing at issue instead of at
+    their wait (an LDS race, a missing wait or a ring slot refilled while
+    still being read would show as a difference)."""
     base = _bf16_step_outputs()
     emu_mode.emu_set_range_mode(1)
     alt = _bf16_step_outputs()
     emu_mode.emu_set_range_mode(0)
     emu_mode.emu_set_reverse_order(1)
     rev = _bf16_step_outputs()
-    for other in (alt, rev):
+    emu_mode.emu_set_reverse_order(0)
+    emu_mode.emu_set_land_early(1)
+    early = _bf16_step_outputs()
+    for other in (alt, rev, early):
         assert other[0] == base[0] and other[1] == base[1]
         for n in base[2]:
             assert np.array_equal(other[2][n], base[2][n]), n
