@@ -109,6 +109,18 @@ bool config_ok(const gpt2_config* c, std::string* why) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Every region is followed by a guard of kGuard bytes of kGuardByte,
+// written by gpt2_create and checked by gpt2_check_arena: a kernel that
+// writes past the end of its region changes them.
+constexpr size_t kGuard = 64;
+constexpr unsigned char kGuardByte = 0xA5;
+
+struct Guard {
+  size_t offset;
+  std::string owner;
+};
+
+
 }  // namespace
 
 // ====================================================================== context
@@ -151,6 +163,10 @@ struct gpt2_ctx {
   bool armed_bwd = false, armed_step = false, grads_fresh = true, poisoned = false;
   std::string err;
 
+  std::vector<Guard> guards;
+  std::vector<unsigned char> guard_host;  // staging for gpt2_check_arena
+  float step_staging = 0.f;               // source of gpt2_set_step_count's copy
+
   int tclass = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
   size_t ev_used = 0;
@@ -171,6 +187,11 @@ namespace {
 struct Planner {
   size_t off = 0;
   std::vector<Tensor>* out;
+  std::vector<Guard>* guards = nullptr;
+  size_t close(size_t end, const std::string& owner) {
+    if (guards) guards->push_back({end, owner});
+    return align256(end + kGuard);
+  }
   size_t add(const std::string& name, int kind, int dtype, std::vector<int64_t> shape, int decay = 0) {
     size_t es = dtype == GPT2_DT_BF16 ? 2 : dtype == GPT2_DT_F64 ? 8 : 4;
     size_t n = 1;
@@ -184,13 +205,13 @@ struct Planner {
     for (int i = 0; i < 4; ++i) t.shape[i] = i < t.ndim ? shape[i] : 0;
     t.offset = off;
     t.bytes = n * es;
-    off = align256(off + t.bytes);
+    off = close(off + t.bytes, name);
     if (out) out->push_back(t);
     return t.offset;
   }
-  size_t raw(size_t bytes) {
+  size_t raw(size_t bytes, const std::string& owner) {
     size_t o = off;
-    off = align256(off + bytes);
+    off = close(off + bytes, owner);
     return o;
   }
 };
@@ -204,6 +225,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   std::vector<Tensor> tmp;
   Planner pl;
   pl.out = x ? &x->tensors : &tmp;
+  pl.guards = x ? &x->guards : nullptr;
   auto specs = param_specs(c);
   const int L = c.n_layer, C = c.n_embd, H = c.n_head;
   const int64_t maxM = (int64_t)c.max_batch * c.max_seq;
@@ -219,9 +241,9 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     n += s.numel();
   }
   size_t nflat = ((n + 63) / 64) * 64;
-  size_t o_par = pl.raw(nflat * 4), o_grad = pl.raw(nflat * 4);
-  size_t o_m = pl.raw(nflat * 4), o_v = pl.raw(nflat * 4);
-  size_t o_sh = bf ? pl.raw(nflat * 2) : 0;
+  size_t o_par = pl.raw(nflat * 4, "parameters"), o_grad = pl.raw(nflat * 4, "gradients");
+  size_t o_m = pl.raw(nflat * 4, "adam_m"), o_v = pl.raw(nflat * 4, "adam_v");
+  size_t o_sh = bf ? pl.raw(nflat * 2, "bf16 weight copies") : 0;
   std::vector<size_t> toff(specs.size(), (size_t)-1);
   std::vector<int> tld(specs.size(), 0);
   size_t nt = 0;
@@ -232,7 +254,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     tld[j] = ld;
     nt += (size_t)specs[j].cols * ld;
   }
-  size_t o_sht = bf ? pl.raw(nt * 2 + 256) : 0;
+  size_t o_sht = bf ? pl.raw(nt * 2 + 256, "transposed bf16 weight copies") : 0;
   // tensor-table views of the flat arrays
   for (size_t j = 0; j < specs.size(); ++j) {
     auto& s = specs[j];
@@ -279,22 +301,22 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t o_dattn = pl.add("d_attn", GPT2_K_ACT, adt, {maxM, C});
   size_t o_dqkv = pl.add("d_qkv", GPT2_K_ACT, adt, {maxM, 3 * C});
   size_t o_du = pl.add("d_fc_u", GPT2_K_ACT, adt, {maxM, 4 * C});
-  size_t o_lnp = pl.raw((size_t)gk::ln_bwd_part_floats((int)maxM, C) * 4);
-  size_t o_colp = pl.raw((size_t)gk::colsum_parts((int)maxM) * 4 * C * 4);
+  size_t o_lnp = pl.raw((size_t)gk::ln_bwd_part_floats((int)maxM, C) * 4, "LayerNorm partials");
+  size_t o_colp = pl.raw((size_t)gk::colsum_parts((int)maxM) * 4 * C * 4, "column-sum partials");
   size_t sk = 0;
   {
     const int64_t shapes[5][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}, {c.padded_vocab, C}};
     for (auto& s : shapes) sk = std::max(sk, gk::gemm_splitk_ws_elems((int)s[0], (int)s[1], (int)maxM));
   }
-  size_t o_sk = pl.raw(sk * 4 + 256);
-  size_t o_emb = pl.raw(gk::embed_bwd_workspace((int)maxM, C));
-  size_t o_attn = pl.raw(gk::attn_bwd_workspace(1, (int)maxM, H) * 4);
-  size_t o_norm = pl.raw(gk::sumsq_blocks() * 8);
+  size_t o_sk = pl.raw(sk * 4 + 256, "split-K partials");
+  size_t o_emb = pl.raw(gk::embed_bwd_workspace((int)maxM, C), "embedding-backward workspace");
+  size_t o_attn = pl.raw(gk::attn_bwd_workspace(1, (int)maxM, H) * 4, "attention workspace");
+  size_t o_norm = pl.raw(gk::sumsq_blocks() * 8, "norm partials");
   // AdamW chunk table
   const size_t CH = 16384;
   size_t nchunks = 0;
   for (auto& s : specs) nchunks += (s.numel() + CH - 1) / CH;
-  size_t o_chunks = pl.raw(nchunks * sizeof(gk::AdamChunk));
+  size_t o_chunks = pl.raw(nchunks * sizeof(gk::AdamChunk), "AdamW chunk table");
   size_t total = pl.off;
 
   if (x) {
@@ -663,6 +685,8 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
   // logits columns [Vp, row stride) are never written by the classifier GEMM
   if ((e = hipMemsetAsync(c->logits, 0, (size_t)c->maxM * c->ldl * c->act_es, c->st)))
     return bail(e, "zero logits");
+  for (const Guard& g : c->guards)
+    if ((e = hipMemsetAsync(c->arena + g.offset, kGuardByte, kGuard, c->st))) return bail(e, "guards");
   if (c->bf && (e = gk::to_bf16(c->params, c->shadow, c->nflat, c->st))) return bail(e, "bf16 copy");
   if (c->bf && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
   if ((e = refresh_transposed(c))) return bail(e, "transposed copies");
@@ -847,6 +871,58 @@ GPT2_API gpt2_status gpt2_block_fwd_bwd(gpt2_ctx* c, int32_t layer, const float*
   HIPCHK(c, gk::copy_f32_to_act(c->dres, c->dres_act, c->bf, (size_t)M * c->C, c->st));
   HIPCHK(c, bwd_layer(c, layer, M, B, T, 0.f));
   HIPCHK(c, hipMemcpyAsync(d_dx, c->dres, bytes, hipMemcpyDeviceToDevice, c->st));
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_check_arena(gpt2_ctx* c, int32_t* n_bad) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  const size_t n = c->guards.size();
+  c->guard_host.assign(n * kGuard, 0);
+  for (size_t i = 0; i < n; ++i)
+    HIPCHK(c, hipMemcpyAsync(c->guard_host.data() + i * kGuard, c->arena + c->guards[i].offset, kGuard,
+                             hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  int32_t bad = 0;
+  std::string first;
+  for (size_t i = 0; i < n; ++i)
+    for (size_t k = 0; k < kGuard; ++k)
+      if (c->guard_host[i * kGuard + k] != kGuardByte) {
+        if (bad++ == 0) first = c->guards[i].owner;
+        break;
+      }
+  if (n_bad) *n_bad = bad;
+  if (bad) return fail(c, GPT2_E_ARENA, "guard after region '" + first + "' overwritten (" +
+                                            std::to_string(bad) + " damaged guards)");
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_sync_weight_copies(gpt2_ctx* c) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (c->bf) HIPCHK(c, gk::to_bf16(c->params, c->shadow, c->nflat, c->st));
+  HIPCHK(c, refresh_transposed(c));
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_get_step_count(gpt2_ctx* c, int64_t* t) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (!t) return fail(c, GPT2_E_ARG, "NULL output");
+  float v = 0.f;
+  HIPCHK(c, hipMemcpyAsync(&v, c->scal + 5, 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  *t = (int64_t)v;
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_set_step_count(gpt2_ctx* c, int64_t t) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (t < 0 || t > (1 << 24)) return fail(c, GPT2_E_ARG, "step count outside [0, 2^24]");
+  c->step_staging = (float)t;
+  HIPCHK(c, hipMemcpyAsync(c->scal + 5, &c->step_staging, 4, hipMemcpyHostToDevice, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
   return GPT2_OK;
 }
 

@@ -29,7 +29,8 @@ TIMING = {"none": 0, "lmhead_fwd": 1, "gemm": 2, "attn_fwd": 3, "attn_bwd": 4, "
 EXPORTS = ["gpt2_default_config", "gpt2_arena_bytes", "gpt2_num_params", "gpt2_init_host",
            "gpt2_create", "gpt2_destroy", "gpt2_last_error", "gpt2_forward", "gpt2_backward",
            "gpt2_zero_grad", "gpt2_step", "gpt2_lr_at", "gpt2_block_fwd_bwd", "gpt2_num_tensors",
-           "gpt2_tensor_info", "gpt2_timing_enable", "gpt2_timing_read"]
+           "gpt2_tensor_info", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_sync_weight_copies",
+           "gpt2_get_step_count", "gpt2_set_step_count", "gpt2_check_arena"]
 
 
 class Config(ct.Structure):
@@ -78,6 +79,10 @@ def bind(L):
         "gpt2_tensor_info": (I32, [P, I32, ct.POINTER(TensorDesc)]),
         "gpt2_timing_enable": (I32, [P, I32]),
         "gpt2_timing_read": (I32, [P, ct.POINTER(ct.c_double), ct.POINTER(I64)]),
+        "gpt2_sync_weight_copies": (I32, [P]),
+        "gpt2_get_step_count": (I32, [P, ct.POINTER(I64)]),
+        "gpt2_set_step_count": (I32, [P, I64]),
+        "gpt2_check_arena": (I32, [P, ct.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -210,6 +215,39 @@ class GPT2Step:
         n = ct.c_int64(0)
         self._check(self._L.gpt2_timing_read(self.ctx, ct.byref(ms), ct.byref(n)))
         return ms.value, n.value
+
+    def check_arena(self):
+        """Raises GPT2Error (E_ARENA) if a kernel wrote past its arena region."""
+        n = ct.c_int32(0)
+        self._check(self._L.gpt2_check_arena(self.ctx, ct.byref(n)))
+
+    def sync_weight_copies(self):
+        self._check(self._L.gpt2_sync_weight_copies(self.ctx))
+
+    def step_count(self):
+        t = ct.c_int64(0)
+        self._check(self._L.gpt2_get_step_count(self.ctx, ct.byref(t)))
+        return t.value
+
+    def set_step_count(self, t: int):
+        self._check(self._L.gpt2_set_step_count(self.ctx, t))
+
+    def state_dict(self):
+        """Checkpoint: host copies of the parameters, both AdamW moments and
+        the step count."""
+        kinds = ("param", "adam_m", "adam_v")
+        out = {n: self.view(n).clone().cpu() for n, t in self.tensors.items() if t["kind"] in kinds}
+        out["__step__"] = self.step_count()
+        return out
+
+    def load_state_dict(self, sd):
+        """Resume from state_dict(): writes the tensors back through the
+        arena views, sets the step count and refreshes the bf16 copies."""
+        for n, v in sd.items():
+            if n != "__step__":
+                self.view(n).copy_(v)
+        self.set_step_count(sd["__step__"])
+        self.sync_weight_copies()
 
     # ------------------------------------------------------------------ views
     def view(self, name):

@@ -179,6 +179,28 @@ double gpt2_lr_at(int64_t it, double max_lr, double min_lr, int64_t warmup, int6
 gpt2_status gpt2_block_fwd_bwd(gpt2_ctx* c, int32_t layer, const float* d_x, const float* d_dy,
                                float* d_y, float* d_dx, int32_t B, int32_t T);
 
+/* Checkpoint and resume.  A checkpoint is the fp32 parameters, both AdamW
+ * moments (tensor kinds GPT2_K_PARAM, GPT2_K_ADAM_M, GPT2_K_ADAM_V, read and
+ * written through the tensor table's views) and the optimizer step count.
+ * After writing parameters into a context, gpt2_sync_weight_copies rewrites
+ * the bf16 copies (and their transposed copies) that the GEMMs read from the
+ * fp32 parameters; a context resumed this way continues bitwise like the
+ * one that was saved.  The step count t (AdamW's bias corrections use t + 1
+ * at the next step) lives on the device: get synchronizes the stream and
+ * reads it, set (0 <= t <= 2^24) writes it and synchronizes. */
+gpt2_status gpt2_sync_weight_copies(gpt2_ctx* c);
+gpt2_status gpt2_get_step_count(gpt2_ctx* c, int64_t* t);
+gpt2_status gpt2_set_step_count(gpt2_ctx* c, int64_t t);
+
+/* Arena guards: the layout leaves 64 bytes of 0xA5 after every region
+ * (tensor or workspace), written by gpt2_create.  gpt2_check_arena
+ * synchronizes the stream and reads them back.  GPT2_OK if every guard is
+ * intact; otherwise GPT2_E_ARENA, gpt2_last_error names the region before
+ * the first damaged guard, and *n_bad (host, nullable) counts the damaged
+ * guards.  A debugging aid for kernels that write past their region; not
+ * needed for normal use. */
+gpt2_status gpt2_check_arena(gpt2_ctx* c, int32_t* n_bad);
+
 /* Introspection: zero-copy views into the arena. */
 int32_t gpt2_num_tensors(const gpt2_ctx* c);
 gpt2_status gpt2_tensor_info(const gpt2_ctx* c, int32_t i, gpt2_tensor_desc* out);

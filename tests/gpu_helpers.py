@@ -124,6 +124,7 @@ def run_step(p, B, T, seed=0, data_seed=1, lr=6e-4, dt=np.float64, micro=1, be: 
     norm = m.step(lr, 1.0)
     gg = gpu_grads(m, names)
     pp = gpu_params(m, names)
+    m.check_arena()
     m.close()
     P = oracle_init(oc, seed)
     ref = O.train_step(P, batches, oc, lr=lr, clip=1.0, t=1, dt=dt)

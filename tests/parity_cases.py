@@ -187,6 +187,65 @@ def overfit_single_batch_tracks_oracle(be: Backend, steps: int = 25):
     assert gl[-1] < gl[0] - 1.0
 
 
+def checkpoint_resume_bitwise(be: Backend, preset: str):
+    """Save after two steps (parameters, both moments, step count through the
+    tensor table), restore into a fresh context created from another seed,
+    and the third step of both is bitwise the same: loss, norm, parameters,
+    moments and the step count."""
+    p = SMALL_FP32 if preset == "fp32" else SMALL_BF16
+    B, T = 2, 32
+    lc, oc, p = configs(p, B, T)
+    s = stream_for(p, 3 * B * T + 1, 11)
+    batches = [inputs.batch_from_stream(s, B, T, k) for k in range(3)]
+    a = be.make(lc, 0)
+    for x, y in batches[:2]:
+        a.forward(be.dev(x), be.dev(y))
+        a.backward(1.0)
+        a.step(1e-3)
+    sd = a.state_dict()
+    assert sd["__step__"] == 2
+    x, y = batches[2]
+    la = a.forward(be.dev(x), be.dev(y))
+    a.backward(1.0)
+    na = a.step(1e-3)
+    ra = a.state_dict()
+    a.check_arena()
+    a.close()
+    b = be.make(lc, 7)
+    b.load_state_dict(sd)
+    lb = b.forward(be.dev(x), be.dev(y))
+    b.backward(1.0)
+    nb = b.step(1e-3)
+    rb = b.state_dict()
+    b.check_arena()
+    b.close()
+    assert la == lb and na == nb
+    assert ra["__step__"] == rb["__step__"] == 3
+    for n in ra:
+        if n != "__step__":
+            assert torch.equal(ra[n], rb[n]), n
+
+
+def arena_guard_detects_overrun(be: Backend):
+    """The guards after the arena regions are intact after a step, and one
+    byte changed right after a region's end is reported, naming the region."""
+    import pytest
+    lc, oc, p = configs(SMALL_BF16, 2, 16)
+    m = be.make(lc, 0)
+    x, y = inputs.batch_from_stream(stream_for(p, 33, 3), 2, 16)
+    m.forward(be.dev(x), be.dev(y))
+    m.backward(1.0)
+    m.step(1e-3)
+    m.check_arena()
+    t = m.tensors["losses"]
+    end = t["offset"] + t["bytes"]
+    m.arena[end + 5] = 0
+    with pytest.raises(G.GPT2Error) as e:
+        m.check_arena()
+    assert e.value.status == G.GPT2_E_ARENA and "losses" in str(e.value)
+    m.close()
+
+
 # ---------------------------------------------------------------------------- GPT-2 124M shapes
 
 def block_124m(be: Backend, B: int = 16, T: int = 1024):
@@ -203,6 +262,7 @@ def block_124m(be: Backend, B: int = 16, T: int = 1024):
     dx = dx.cpu().numpy()
     names = [n for n in m.param_names() if n.startswith("h0.")]
     gg = gpu_grads(m, names)
+    m.check_arena()
     m.close()
     P = oracle_init(oc, 0)
     Pl = {n: P[n] for n in names}
@@ -239,6 +299,7 @@ def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6
     norm = m.step(lr, 1.0)
     gg = gpu_grads(m, names)
     pp = gpu_params(m, names)
+    m.check_arena()
     m.close()
     assert abs(loss - float(np.mean(per, dtype=np.float64))) <= 1e-5 * loss
     ref = O.train_step(oracle_init(oc, 0), _one_sequence_batches(x, y), oc, lr=lr, clip=1.0, t=1,
@@ -266,6 +327,7 @@ def accumulated_step_vs_oracle(be: Backend, B: int = 32, T: int = 512, micro: in
     norm = m.step(lr, 1.0)
     gg = gpu_grads(m, names)
     pp = gpu_params(m, names)
+    m.check_arena()
     m.close()
     seqs = []
     for x, y in batches:

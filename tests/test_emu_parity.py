@@ -103,3 +103,12 @@ def test_emu_error_paths():
 
 def test_emu_overfit_single_batch_tracks_oracle():
     cases.overfit_single_batch_tracks_oracle(EMU, steps=12)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_emu_checkpoint_resume_bitwise(preset):
+    cases.checkpoint_resume_bitwise(EMU, preset)
+
+
+def test_emu_arena_guard_detects_overrun():
+    cases.arena_guard_detects_overrun(EMU)

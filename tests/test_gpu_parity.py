@@ -51,3 +51,12 @@ def test_error_paths():
 
 def test_overfit_single_batch_tracks_oracle():
     cases.overfit_single_batch_tracks_oracle(GPU)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_checkpoint_resume_bitwise(preset):
+    cases.checkpoint_resume_bitwise(GPU, preset)
+
+
+def test_arena_guard_detects_overrun():
+    cases.arena_guard_detects_overrun(GPU)
