@@ -16,6 +16,13 @@
 #include <thread>
 #include <vector>
 
+#if defined(__has_feature)
+#if __has_feature(address_sanitizer)
+#define EMU_ASAN 1
+#include <sanitizer/common_interface_defs.h>
+#endif
+#endif
+
 extern "C" void emu_switch(void** save_sp, void* load_sp);
 extern "C" void emu_fiber_tramp();
 extern "C" void emu_fiber_main();
@@ -88,7 +95,11 @@ unsigned char* new_stack() {
   return (unsigned char*)p + pg;
 }
 
-void to_sched() { emu_switch(&W->current->sp, W->sched_sp); }
+// Stack switches, announced to AddressSanitizer in sanitized builds.
+void switch_to_fiber(Fiber& f);
+void switch_to_sched(Fiber* f);
+
+void to_sched() { switch_to_sched(W->current); }
 
 void complete_wave(int wave) {
   WaveState& w = W->waves[wave];
@@ -155,7 +166,7 @@ void run_block() {
       Fiber& f = W->fibers[i];
       if (f.state != RUN) continue;
       W->current = &f;
-      emu_switch(&W->sched_sp, f.sp);
+      switch_to_fiber(f);
       ran = true;
     }
     if (!ran && W->alive > 0) describe_and_die("deadlock (divergent barrier or wave operation)");
@@ -167,6 +178,37 @@ void run_block() {
         for (auto& pw : g) std::memcpy(pw.dst, pw.data, pw.n);
       W->waves[wv].q.clear();
     }
+}
+
+#ifdef EMU_ASAN
+thread_local void* t_sched_fake = nullptr;
+thread_local const void* t_sched_bottom = nullptr;
+thread_local size_t t_sched_size = 0;
+#endif
+
+// Protocol of the sanitizer's fiber interface: the side that leaves calls
+// start (saving its fake stack, naming the destination stack), the side that
+// resumes calls finish (restoring its fake stack, learning the bounds of the
+// stack it came from).  Fibers learn the scheduler's stack bounds that way.
+void switch_to_fiber(Fiber& f) {
+#ifdef EMU_ASAN
+  __sanitizer_start_switch_fiber(&t_sched_fake, W->stacks[f.lin], STACK);
+  emu_switch(&W->sched_sp, f.sp);
+  __sanitizer_finish_switch_fiber(t_sched_fake, nullptr, nullptr);
+#else
+  emu_switch(&W->sched_sp, f.sp);
+#endif
+}
+
+void switch_to_sched(Fiber* f) {
+#ifdef EMU_ASAN
+  void* fake = nullptr;
+  __sanitizer_start_switch_fiber(f->state == DEAD ? nullptr : &fake, t_sched_bottom, t_sched_size);
+  emu_switch(&f->sp, W->sched_sp);
+  __sanitizer_finish_switch_fiber(fake, &t_sched_bottom, &t_sched_size);
+#else
+  emu_switch(&f->sp, W->sched_sp);
+#endif
 }
 
 // ------------------------------------------------------------------ worker pool
@@ -479,6 +521,9 @@ void run_grid(dim3 grid, dim3 block, size_t shmem, BlockThunk thunk, void* args)
 
 extern "C" void emu_fiber_main() {
   using namespace emu;
+#ifdef EMU_ASAN
+  __sanitizer_finish_switch_fiber(nullptr, &t_sched_bottom, &t_sched_size);
+#endif
   W->thunk(W->args);
   Fiber* f = W->current;
   f->state = DEAD;
@@ -487,7 +532,7 @@ extern "C" void emu_fiber_main() {
   --w.alive;
   if (w.arrived > 0 && w.arrived == w.alive) complete_wave(f->wave);
   if (W->at_barrier > 0 && W->at_barrier == W->alive) release_barrier();
-  emu_switch(&f->sp, W->sched_sp);
+  switch_to_sched(f);
   fatal("dead fiber resumed");
 }
 
