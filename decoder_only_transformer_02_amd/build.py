@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgpt2mi.so")
-SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "engine.hip"]
+SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "decode.hip", "engine.hip"]
 ARCH = "gfx950"
 
 

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_embed_fwd(const int32_t* __restrict__ t
                                                    const float* __restrict__ wte,
                                                    const float* __restrict__ wpe,
                                                    float* __restrict__ h, int M, int T, int C,
-                                                   int V, int* flag) {
+                                                   int V, int* flag, int pos0) {
   int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void k_embed_fwd(const int32_t* __restrict__ t
     if (lane == 0) atomicOr(flag, FLAG_TOKEN);
     id = id < 0 ? 0 : V - 1;
   }
-  int t = row % T;
+  int t = pos0 + row % T;
   const float4* a = (const float4*)(wte + (size_t)id * C);
   const float4* b = (const float4*)(wpe + (size_t)t * C);
   float4* o = (float4*)(h + (size_t)row * C);
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void k_embed_fwd(const int32_t* __restrict__ t
 }
 
 hipError_t embed_fwd(const int32_t* tok, const float* wte, const float* wpe, float* h, int M, int T,
-                     int C, int V, int* flag, hipStream_t st) {
-  k_embed_fwd<<<cdiv(M, 4), 256, 0, st>>>(tok, wte, wpe, h, M, T, C, V, flag);
+                     int C, int V, int* flag, hipStream_t st, int pos0) {
+  k_embed_fwd<<<cdiv(M, 4), 256, 0, st>>>(tok, wte, wpe, h, M, T, C, V, flag, pos0);
   return hipGetLastError();
 }
 

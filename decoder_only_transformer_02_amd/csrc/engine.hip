@@ -436,8 +436,17 @@ hipError_t run_gemm(gpt2_ctx* c, const GemmArgs& a, int tcls = GPT2_T_GEMM) {
     if (e_ != hipSuccess) return e_;    \
   } while (0)
 
-// One transformer block forward: h[2l] -> h[2l+1] -> h[2l+2].
-hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T) {
+// Attention of one decode step: the newest position t of each of B
+// sequences against the layer's key/value cache (positions 0..t).
+struct DecodeAttn {
+  void* cache;  // this layer's [max_batch][max_seq][2][C]
+  int t;
+};
+
+// One transformer block forward: h[2l] -> h[2l+1] -> h[2l+2].  With `dec`
+// the rows are one new position per sequence (M = B) whose keys and values
+// are appended to the cache and whose queries attend over it.
+hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T, const DecodeAttn* dec = nullptr) {
   const int C = c->C;
   const float eps = c->cfg.ln_eps;
   {
@@ -449,7 +458,11 @@ hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T) {
                          gk::EPI_STORE, c->qkv[l], 3 * C);
   g.bias = c->P(c->li(l, 3));
   KCHK(run_gemm(c, g));
-  {
+  if (dec) {
+    KCHK(gk::kv_store(c->qkv[l], dec->cache, B, 1, dec->t, c->cfg.max_seq, C, c->bf, c->st));
+    KCHK(gk::attn_decode(c->qkv[l], dec->cache, c->att[l], B, c->H, c->hd, c->cfg.max_seq, dec->t + 1, c->bf,
+                         c->st));
+  } else {
     Timed t(c, GPT2_T_ATTN_FWD);
     KCHK(gk::attn_fwd(c->qkv[l], c->att[l], c->lse[l], B, T, c->H, c->hd, c->bf, c->st));
   }
@@ -554,6 +567,37 @@ hipError_t refresh_transposed(gpt2_ctx* c) {
     const auto& sp = c->specs[j];
     KCHK(gk::transpose_bf16(c->shadow + c->poff[j], (int)sp.rows, (int)sp.cols,
                             c->shadow_t + c->toff[j], c->tld[j], c->st));
+  }
+  return hipSuccess;
+}
+
+// The forward schedule over the ids already in c->tok ([B, T] packed):
+// embeddings, the L blocks, the final LayerNorm and the classifier; with
+// targets also the per-position losses (and, when want_grad, the logits
+// gradient in place) and the mean loss in scal[8].
+hipError_t run_forward(gpt2_ctx* c, int B, int T, const int32_t* d_targets, bool want_grad) {
+  const int M = B * T, C = c->C;
+  {
+    Timed t(c, GPT2_T_EMBED);
+    KCHK(gk::embed_fwd(c->tok, c->P(0), c->P(1), c->h[0], M, T, C, c->V, c->flag, c->st));
+  }
+  for (int l = 0; l < c->L; ++l) KCHK(fwd_layer(c, l, M, B, T));
+  const int lf = 2 + 12 * c->L;
+  {
+    Timed t(c, GPT2_T_LN_FWD);
+    KCHK(gk::ln_fwd(c->h[2 * c->L], c->P(lf), c->P(lf + 1), c->ln[2 * c->L], c->bf, c->mean[2 * c->L],
+                    c->rstd[2 * c->L], M, C, c->cfg.ln_eps, c->st));
+  }
+  GemmArgs g = gemm_args(c, M, c->Vp, C, c->ln[2 * c->L], C, false, c->W(0), C, false, gk::EPI_LOGITS,
+                         c->logits, c->ldl);
+  KCHK(run_gemm(c, g, GPT2_T_LMHEAD_FWD));
+  if (d_targets) {
+    {
+      Timed t(c, GPT2_T_XENT);
+      KCHK(gk::xent(c->logits, c->bf, c->ldl, c->Vp, c->V, d_targets, c->losses, 1.0f / (float)M, want_grad,
+                    M, c->flag, c->st));
+    }
+    KCHK(gk::loss_reduce(c->losses, M, c->scal + 8, c->flag, c->st));
   }
   return hipSuccess;
 }
@@ -727,53 +771,110 @@ GPT2_API const char* gpt2_last_error(const gpt2_ctx* c) {
   return c->err.c_str();
 }
 
-GPT2_API gpt2_status gpt2_forward(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
-                                  int32_t B, int32_t T, float* h_loss) {
+namespace {
+
+// Loss readback shared by forward and evaluation: the flags decide the
+// status (ids or targets outside the vocabulary, a non-finite loss).
+gpt2_status finish_loss(gpt2_ctx* c, const int32_t* d_targets, float* h_loss) {
+  int flags = 0;
+  if (d_targets) HIPCHK(c, hipMemcpyAsync(h_loss, c->scal + 8, 4, hipMemcpyDeviceToHost, c->st));
+  gpt2_status s = read_flags(c, &flags);
+  if (s) return s;
+  if (flags & 3) {
+    c->armed_bwd = false;
+    return fail(c, GPT2_E_TOKEN, "token id or target outside [0, vocab_size)");
+  }
+  if (flags & 4) return fail(c, GPT2_E_NONFINITE, "non-finite loss");
+  return GPT2_OK;
+}
+
+gpt2_status start_forward(gpt2_ctx* c, const int32_t* d_tokens, int32_t B, int32_t T) {
   gpt2_status s = check_ctx(c);
   if (s) return s;
   if (!d_tokens) return fail(c, GPT2_E_ARG, "tokens is NULL");
   if (B < 1 || T < 1 || T > c->cfg.max_seq || (int64_t)B * T > c->maxM)
     return fail(c, GPT2_E_SHAPE, "B*T exceeds the arena or T > max_seq");
-  const int M = B * T, C = c->C;
   c->armed_bwd = false;
   c->B = B;
   c->T = T;
   HIPCHK(c, hipMemsetAsync(c->flag, 0, 16, c->st));
-  HIPCHK(c, hipMemcpyAsync(c->tok, d_tokens, (size_t)M * 4, hipMemcpyDeviceToDevice, c->st));
-  {
-    Timed t(c, GPT2_T_EMBED);
-    HIPCHK(c, gk::embed_fwd(c->tok, c->P(0), c->P(1), c->h[0], M, T, C, c->V, c->flag, c->st));
-  }
-  for (int l = 0; l < c->L; ++l) HIPCHK(c, fwd_layer(c, l, M, B, T));
-  const int lf = 2 + 12 * c->L;
-  {
-    Timed t(c, GPT2_T_LN_FWD);
-    HIPCHK(c, gk::ln_fwd(c->h[2 * c->L], c->P(lf), c->P(lf + 1), c->ln[2 * c->L], c->bf,
-                         c->mean[2 * c->L], c->rstd[2 * c->L], M, C, c->cfg.ln_eps, c->st));
-  }
-  GemmArgs g = gemm_args(c, M, c->Vp, C, c->ln[2 * c->L], C, false, c->W(0), C, false,
-                         gk::EPI_LOGITS, c->logits, c->ldl);
-  HIPCHK(c, run_gemm(c, g, GPT2_T_LMHEAD_FWD));
-  if (d_targets) {
-    {
-      Timed t(c, GPT2_T_XENT);
-      HIPCHK(c, gk::xent(c->logits, c->bf, c->ldl, c->Vp, c->V, d_targets, c->losses,
-                         1.0f / (float)M, true, M, c->flag, c->st));
+  HIPCHK(c, hipMemcpyAsync(c->tok, d_tokens, (size_t)B * T * 4, hipMemcpyDeviceToDevice, c->st));
+  return GPT2_OK;
+}
+
+}  // namespace
+
+GPT2_API gpt2_status gpt2_forward(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
+                                  int32_t B, int32_t T, float* h_loss) {
+  gpt2_status s = start_forward(c, d_tokens, B, T);
+  if (s) return s;
+  HIPCHK(c, run_forward(c, B, T, d_targets, true));
+  if (d_targets) c->armed_bwd = true;
+  if (h_loss) return finish_loss(c, d_targets, h_loss);
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_eval_loss(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
+                                    int32_t B, int32_t T, float* h_loss) {
+  if (c && !d_targets) return fail(c, GPT2_E_ARG, "targets is NULL");
+  gpt2_status s = start_forward(c, d_tokens, B, T);
+  if (s) return s;
+  HIPCHK(c, run_forward(c, B, T, d_targets, false));
+  if (h_loss) return finish_loss(c, d_targets, h_loss);
+  return GPT2_OK;
+}
+
+GPT2_API size_t gpt2_kv_cache_bytes(const gpt2_config* cfg) {
+  if (!config_ok(cfg, nullptr)) return 0;
+  const size_t es = cfg->compute == GPT2_BF16 ? 2 : 4;
+  return (size_t)cfg->n_layer * cfg->max_batch * cfg->max_seq * 2 * cfg->n_embd * es;
+}
+
+GPT2_API gpt2_status gpt2_generate(gpt2_ctx* c, void* d_kv_cache, size_t kv_bytes, int32_t* d_tokens,
+                                   int32_t B, int32_t T0, int32_t T_total, const float* d_uniform,
+                                   float* d_logprob) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (!d_kv_cache || !d_tokens || !d_uniform) return fail(c, GPT2_E_ARG, "NULL buffer");
+  if (kv_bytes < gpt2_kv_cache_bytes(&c->cfg)) return fail(c, GPT2_E_ARENA, "key/value cache too small");
+  if (B < 1 || B > c->cfg.max_batch || T0 < 1 || T_total <= T0 || T_total > c->cfg.max_seq)
+    return fail(c, GPT2_E_SHAPE, "need 1 <= B <= max_batch and 1 <= T0 < T_total <= max_seq");
+  const int C = c->C, L = c->L, n_new = T_total - T0;
+  const size_t layer_bytes = (size_t)c->cfg.max_batch * c->cfg.max_seq * 2 * C * c->act_es;
+  auto cache = [&](int l) { return (void*)((char*)d_kv_cache + (size_t)l * layer_bytes); };
+  c->armed_bwd = false;
+  HIPCHK(c, hipMemsetAsync(c->flag, 0, 16, c->st));
+  // prefill: the prefix through the ordinary forward, its keys and values
+  // into the cache, then the first new token from the last prefix position
+  HIPCHK(c, hipMemcpy2DAsync(c->tok, (size_t)T0 * 4, d_tokens, (size_t)T_total * 4, (size_t)T0 * 4, B,
+                             hipMemcpyDeviceToDevice, c->st));
+  HIPCHK(c, run_forward(c, B, T0, nullptr, false));
+  for (int l = 0; l < L; ++l) HIPCHK(c, gk::kv_store(c->qkv[l], cache(l), B, T0, 0, c->cfg.max_seq, C, c->bf, c->st));
+  HIPCHK(c, gk::sample(c->logits, c->bf, c->ldl, T0, T0 - 1, c->V, B, d_uniform, n_new, d_tokens + T0, T_total,
+                       d_logprob, n_new, c->st));
+  // decode: one position per sequence per step, attention over the cache
+  const int lf = 2 + 12 * L;
+  for (int t = T0; t < T_total - 1; ++t) {
+    HIPCHK(c, hipMemcpy2DAsync(c->tok, 4, d_tokens + t, (size_t)T_total * 4, 4, B, hipMemcpyDeviceToDevice,
+                               c->st));
+    HIPCHK(c, gk::embed_fwd(c->tok, c->P(0), c->P(1), c->h[0], B, 1, C, c->V, c->flag, c->st, t));
+    for (int l = 0; l < L; ++l) {
+      DecodeAttn d{cache(l), t};
+      HIPCHK(c, fwd_layer(c, l, B, B, 1, &d));
     }
-    HIPCHK(c, gk::loss_reduce(c->losses, M, c->scal + 8, c->flag, c->st));
-    c->armed_bwd = true;
+    HIPCHK(c, gk::ln_fwd(c->h[2 * L], c->P(lf), c->P(lf + 1), c->ln[2 * L], c->bf, c->mean[2 * L],
+                         c->rstd[2 * L], B, C, c->cfg.ln_eps, c->st));
+    GemmArgs g = gemm_args(c, B, c->Vp, C, c->ln[2 * L], C, false, c->W(0), C, false, gk::EPI_LOGITS, c->logits,
+                           c->ldl);
+    HIPCHK(c, run_gemm(c, g));
+    const int k = t + 1 - T0;
+    HIPCHK(c, gk::sample(c->logits, c->bf, c->ldl, 1, 0, c->V, B, d_uniform + k, n_new, d_tokens + t + 1,
+                         T_total, d_logprob ? d_logprob + k : nullptr, n_new, c->st));
   }
-  if (h_loss) {
-    int flags = 0;
-    if (d_targets) HIPCHK(c, hipMemcpyAsync(h_loss, c->scal + 8, 4, hipMemcpyDeviceToHost, c->st));
-    s = read_flags(c, &flags);
-    if (s) return s;
-    if (flags & 3) {
-      c->armed_bwd = false;
-      return fail(c, GPT2_E_TOKEN, "token id or target outside [0, vocab_size)");
-    }
-    if (flags & 4) return fail(c, GPT2_E_NONFINITE, "non-finite loss");
-  }
+  int flags = 0;
+  s = read_flags(c, &flags);
+  if (s) return s;
+  if (flags & 1) return fail(c, GPT2_E_TOKEN, "prefix id outside [0, vocab_size)");
   return GPT2_OK;
 }
 

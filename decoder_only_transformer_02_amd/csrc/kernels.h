@@ -8,9 +8,9 @@
 namespace gk {
 
 // ---------------------------------------------------------------- elementwise
-// h[m, :] = wte[clamp(tok[m]), :] + wpe[m % T, :]; flags bad ids in *flag.
+// h[m, :] = wte[clamp(tok[m]), :] + wpe[pos0 + m % T, :]; flags bad ids in *flag.
 hipError_t embed_fwd(const int32_t* tok, const float* wte, const float* wpe, float* h, int M, int T,
-                     int C, int V, int* flag, hipStream_t st);
+                     int C, int V, int* flag, hipStream_t st, int pos0 = 0);
 // LayerNorm forward of fp32 rows; y in the activation type (bf16 when
 // y_bf16, else fp32); mean / rstd per row.
 hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, bool y_bf16, float* mean,
@@ -109,5 +109,20 @@ hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, i
 size_t attn_bwd_workspace(int B, int T, int H);
 hipError_t attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, void* dqkv,
                     float* ws, int B, int T, int H, int hd, bool bf16, hipStream_t st);
+
+// ---------------------------------------------------------------- sampling with a key/value cache
+// cache[b][t0 + i][0:2C] = qkv[b * n + i][C:3C] (keys and values of n new
+// positions of B sequences; cache rows of max_seq positions).
+hipError_t kv_store(const void* qkv, void* cache, int B, int n, int t0, int Tmax, int C, bool bf,
+                    hipStream_t st);
+// out[b] = attention of query qkv[b][0:C] over the keys / values of cache
+// positions 0 .. nkeys-1 of sequence b.
+hipError_t attn_decode(const void* qkv, const void* cache, void* out, int B, int H, int hd, int Tmax, int nkeys,
+                       bool bf, hipStream_t st);
+// tok[b * tok_stride] = inverse-CDF sample of softmax(z[0:V]) at u[b * u_stride]
+// for the logits row b * row_stride + row0; logprob (nullable) gets its
+// log-probability.
+hipError_t sample(const void* logits, bool bf, int ld, int row_stride, int row0, int V, int B, const float* u,
+                  int u_stride, int32_t* tok, int tok_stride, float* logprob, int lp_stride, hipStream_t st);
 
 }  // namespace gk

@@ -30,7 +30,8 @@ EXPORTS = ["gpt2_default_config", "gpt2_arena_bytes", "gpt2_num_params", "gpt2_i
            "gpt2_create", "gpt2_destroy", "gpt2_last_error", "gpt2_forward", "gpt2_backward",
            "gpt2_zero_grad", "gpt2_step", "gpt2_lr_at", "gpt2_block_fwd_bwd", "gpt2_num_tensors",
            "gpt2_tensor_info", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_sync_weight_copies",
-           "gpt2_get_step_count", "gpt2_set_step_count", "gpt2_check_arena"]
+           "gpt2_get_step_count", "gpt2_set_step_count", "gpt2_check_arena", "gpt2_eval_loss",
+           "gpt2_kv_cache_bytes", "gpt2_generate"]
 
 
 class Config(ct.Structure):
@@ -83,6 +84,9 @@ def bind(L):
         "gpt2_get_step_count": (I32, [P, ct.POINTER(I64)]),
         "gpt2_set_step_count": (I32, [P, I64]),
         "gpt2_check_arena": (I32, [P, ct.POINTER(I32)]),
+        "gpt2_eval_loss": (I32, [P, P, P, I32, I32, ct.POINTER(F)]),
+        "gpt2_kv_cache_bytes": (SZ, [cfgp]),
+        "gpt2_generate": (I32, [P, P, SZ, P, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -185,6 +189,30 @@ class GPT2Step:
                                 B, T, ct.byref(loss) if sync else None)
         self._check(st)
         return loss.value if (sync and targets is not None) else None
+
+    def eval_loss(self, tokens, targets, sync=True):
+        """Forward-only mean cross-entropy (no logits gradient, backward not
+        armed)."""
+        B, T = tokens.shape
+        loss = ct.c_float(0.0)
+        self._check(self._L.gpt2_eval_loss(self.ctx, ct.c_void_p(tokens.data_ptr()),
+                                           ct.c_void_p(targets.data_ptr()), B, T,
+                                           ct.byref(loss) if sync else None))
+        return loss.value if sync else None
+
+    def generate(self, tokens, T0, uniforms, logprobs=None):
+        """Samples positions [T0, T) of the int32 [B, T] device tensor
+        `tokens` in place from its prefix [0, T0), with the float32 [B, T - T0]
+        uniform draws; fills `logprobs` (same shape, optional).  The key/value
+        cache is allocated once per context (gpt2_kv_cache_bytes)."""
+        B, T = tokens.shape
+        if getattr(self, "_kv", None) is None:
+            n = self._L.gpt2_kv_cache_bytes(ct.byref(self.cfg))
+            self._kv = self.torch.empty(n, dtype=self.torch.uint8, device=self.device)
+        self._check(self._L.gpt2_generate(self.ctx, ct.c_void_p(self._kv.data_ptr()), self._kv.numel(),
+                                          ct.c_void_p(tokens.data_ptr()), B, T0, T,
+                                          ct.c_void_p(uniforms.data_ptr()),
+                                          ct.c_void_p(logprobs.data_ptr()) if logprobs is not None else None))
 
     def backward(self, grad_scale=1.0):
         self._check(self._L.gpt2_backward(self.ctx, grad_scale))

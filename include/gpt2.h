@@ -143,6 +143,41 @@ const char* gpt2_last_error(const gpt2_ctx* c);
 gpt2_status gpt2_forward(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
                          int32_t B, int32_t T, float* h_loss);
 
+/* Forward-only loss ("Let's reproduce GPT-2 (124M)" chapter "validation
+ * data split, validation loss, sampling revive"): the same forward and
+ * per-position cross-entropy as gpt2_forward with targets (d_targets is
+ * required), but the logits are left in place (no gradient is written) and
+ * backward is not armed; a backward armed by an earlier forward is
+ * disarmed, since its activations are overwritten.  h_loss as in
+ * gpt2_forward. */
+gpt2_status gpt2_eval_loss(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
+                           int32_t B, int32_t T, float* h_loss);
+
+/* Autoregressive sampling with a key/value cache (same video, chapters
+ * "sampling init, prefix tokens" and "sampling loop").
+ * d_tokens: device int32 [B, T_total] row-major; positions [0, T0) hold the
+ * prefix on entry, positions [T0, T_total) receive the sampled tokens.
+ * d_uniform: device float [B, T_total - T0], the uniform draw in [0, 1) for
+ * each new token (the caller supplies the randomness; values outside are
+ * clamped).  Token t is the smallest id v < vocab_size whose cumulative
+ * softmax probability (ids in increasing order, over the vocab_size real
+ * ids: padding ids are never sampled, temperature 1, no truncation) exceeds
+ * the draw.  d_logprob (device float [B, T_total - T0], nullable) receives
+ * each sampled token's log-probability under that softmax.
+ * d_kv_cache: caller-owned device memory of gpt2_kv_cache_bytes(cfg) bytes
+ * (per layer [max_batch][max_seq][2][C] keys and values in the activation
+ * type); kv_bytes its size.  Needs 1 <= B <= max_batch and
+ * 1 <= T0 < T_total <= max_seq.  The prefix runs through the ordinary
+ * forward (its keys and values are then copied to the cache); each later
+ * position runs one row per sequence through the blocks, appending its
+ * keys and values and attending over the cache.  Overwrites the
+ * activations (a pending backward is disarmed); does not touch gradients or
+ * optimizer state.  Synchronizes the stream once at the end;
+ * GPT2_E_TOKEN if a prefix id is outside [0, vocab_size). */
+size_t gpt2_kv_cache_bytes(const gpt2_config* cfg);
+gpt2_status gpt2_generate(gpt2_ctx* c, void* d_kv_cache, size_t kv_bytes, int32_t* d_tokens, int32_t B,
+                          int32_t T0, int32_t T_total, const float* d_uniform, float* d_logprob);
+
 /* Backward of grad_scale * loss (grad_scale 1, or 1/k for k accumulation
  * micro-steps).  The first backward after create / step / zero_grad writes
  * the gradients; later ones add to them. */

@@ -29,7 +29,10 @@ scale 1/sqrt(head_dim) with query i seeing keys j <= i; q, k, v as the
 three contiguous thirds of the qkv projection, heads as contiguous chunks;
 weights stored [out, in]; clip coefficient min(1, clip / (norm + 1e-6));
 decoupled weight decay lr * wd * p; residual projections initialised with
-std 0.02 / sqrt(2 * n_layer).
+std 0.02 / sqrt(2 * n_layer); sampling draws token t from the softmax over
+the vocab_size real ids (padding ids excluded, temperature 1, no
+truncation) by the inverse of its cumulative distribution in id order at a
+uniform draw that the caller supplies.
 
 Precision: every function takes a storage dtype.  float64 (default) is the
 reference for small configurations and finite differences; float32 storage
@@ -491,3 +494,49 @@ def block_fwd_bwd(x, dy, P, l, cfg: Config, dt=F64):
              if name.startswith(f"h{l}.")}
     dx = block_bwd(dy.astype(dt), cache, P, l, cfg, dt, grads)
     return y, dx, grads
+
+
+# ----------------------------------------------------------------------------
+# forward-only workloads: validation loss and sampling ("Let's reproduce
+# GPT-2 (124M)" chapters "sampling init, prefix tokens", "sampling loop" and
+# "validation data split, validation loss, sampling revive")
+# ----------------------------------------------------------------------------
+
+def eval_loss(P, idx, targets, cfg: Config, dt=F64) -> float:
+    """Mean cross-entropy of a batch, forward only (the loss of forward())."""
+    loss, _, _ = forward(P, idx, targets, cfg, dt, keep_logits=False)
+    return loss
+
+
+def sample_token(z_row, u: float, vocab_size: int):
+    """Next token from one row of logits and a uniform draw u in [0, 1):
+    p = softmax(z[:vocab_size]) in float64 (padding ids are not tokens), and
+    the token is the smallest id v with p_0 + ... + p_v > u, i.e. the
+    inverse of the cumulative distribution in id order.  Returns (token,
+    log p_token)."""
+    z = np.asarray(z_row[:vocab_size], dtype=F64)
+    z = z - z.max()
+    e = np.exp(z)
+    S = e.sum()
+    c = np.cumsum(e) / S
+    v = int(np.searchsorted(c, u, side="right"))
+    v = min(v, vocab_size - 1)
+    while e[v] == 0.0 and v > 0:  # the top of the distribution: last id with mass
+        v -= 1
+    return v, float(z[v] - math.log(S))
+
+
+def generate(P, tokens, T0: int, uniforms, cfg: Config, dt=F64):
+    """Autoregressive sampling, the plain way: for t = T0 .. T-1 run the whole
+    forward over positions [0, t) and sample token t from the logits of
+    position t-1 with uniforms[:, t - T0].  tokens: int [B, T] with the
+    prefix in [:, :T0].  Returns (tokens, log-probabilities [B, T - T0])."""
+    tok = np.array(tokens, dtype=np.int64, copy=True)
+    B, T = tok.shape
+    lp = np.zeros((B, T - T0), F64)
+    for t in range(T0, T):
+        _, _, cache = forward(P, tok[:, :t], None, cfg, dt)
+        z = cache["z"].reshape(B, t, -1)[:, t - 1]
+        for b in range(B):
+            tok[b, t], lp[b, t - T0] = sample_token(z[b], float(uniforms[b, t - T0]), cfg.vocab_size)
+    return tok, lp

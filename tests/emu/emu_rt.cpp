@@ -570,6 +570,13 @@ hipError_t hipMemsetAsync(void* dst, int v, size_t n, hipStream_t) {
   if (n) std::memset(dst, v, n);
   return hipSuccess;
 }
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                            size_t height, hipMemcpyKind, hipStream_t) {
+  if (width > dpitch || width > spitch) return hipErrorInvalidValue;
+  for (size_t r = 0; r < height; ++r)
+    std::memmove((char*)dst + r * dpitch, (const char*)src + r * spitch, width);
+  return hipSuccess;
+}
 hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 hipError_t hipDeviceSynchronize() { return hipSuccess; }
 hipError_t hipSetDevice(int) { return hipSuccess; }

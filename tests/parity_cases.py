@@ -246,6 +246,87 @@ def arena_guard_detects_overrun(be: Backend):
     m.close()
 
 
+def eval_loss_forward_only(be: Backend, preset: str):
+    """gpt2_eval_loss gives the forward's loss bitwise, leaves the raw logits
+    in place (bitwise those of a forward without targets), does not arm
+    backward, disarms a backward armed before, and matches the oracle."""
+    import pytest
+    p = SMALL_FP32 if preset == "fp32" else SMALL_BF16
+    B, T = 3, 40
+    lc, oc, p = configs(p, B, T)
+    x, y = inputs.batch_from_stream(stream_for(p, B * T + 1, 6), B, T)
+    m = be.make(lc, 0)
+    m.forward(be.dev(x))
+    z_raw = m.view("logits")[:B * T].clone()
+    l_fwd = m.forward(be.dev(x), be.dev(y))
+    l_eval = m.eval_loss(be.dev(x), be.dev(y))
+    assert l_eval == l_fwd
+    assert torch.equal(m.view("logits")[:B * T], z_raw)
+    with pytest.raises(G.GPT2Error) as e:
+        m.backward(1.0)
+    assert e.value.status == G.GPT2_E_STATE
+    m.check_arena()
+    m.close()
+    ref = O.eval_loss(oracle_init(oc, 0), x, y, oc)
+    tol = 1e-4 if preset == "fp32" else 2e-2
+    assert abs(l_eval - ref) <= tol * ref
+
+
+def generate_matches_oracle(be: Backend, preset: str, B: int = 2, T0: int = 7, T: int = 48, n_layer=None):
+    """Sampling with the key/value cache against the oracle by teacher
+    forcing: one oracle forward over the generated sequence gives the logits
+    before every new token; the token must be the oracle's inverse-CDF pick
+    at the step's draw, or lie within `band` of a cumulative-probability
+    boundary (floating point may then decide either way), and its
+    log-probability must match.  The library's own full forward over the
+    output agrees with the cached decode path too.  Prefix unchanged."""
+    p = {"fp32": SMALL_FP32, "bf16": SMALL_BF16, "124m": G124}[preset]
+    band, lp_tol = (1e-5, 1e-4) if preset == "fp32" else (2e-2, 5e-2)
+    over = {} if n_layer is None else {"n_layer": n_layer}
+    lc, oc, p = configs(p, B, T, **over)
+    rng = np.random.default_rng(12)
+    tok = np.zeros((B, T), np.int32)
+    tok[:, :T0] = stream_for(p, B * T0, 8).reshape(B, T0)
+    u = rng.random((B, T - T0)).astype(np.float32)
+    m = be.make(lc, 0)
+    td = be.dev(tok)
+    lpd = be.dev(np.zeros((B, T - T0), np.float32))
+    m.generate(td, T0, be.dev(u), lpd)
+    out = td.cpu().numpy()
+    lp = lpd.cpu().numpy().astype(np.float64)
+    m.forward(be.dev(out))
+    z_lib = m.view("logits")[:B * T, :p["padded_vocab"]].double().cpu().numpy().reshape(B, T, -1)
+    m.check_arena()
+    m.close()
+    assert np.array_equal(out[:, :T0], tok[:, :T0])
+    assert out.min() >= 0 and out.max() < p["vocab_size"]
+    _, _, cache = O.forward(oracle_init(oc, 0), out.astype(np.int64), None, oc,
+                            np.float32 if preset == "124m" else np.float64)
+    z = cache["z"].reshape(B, T, -1)
+    exact = 0
+    for b in range(B):
+        for t in range(T0, T):
+            zr = z[b, t - 1, :p["vocab_size"]]
+            e = np.exp(zr - zr.max())
+            c = np.cumsum(e) / e.sum()
+            v = int(out[b, t])
+            uu = float(u[b, t - T0])
+            lo = c[v - 1] if v > 0 else 0.0
+            assert lo - band <= uu < c[v] + band, (b, t, v, lo, c[v], uu)
+            exact += int(O.sample_token(zr, uu, p["vocab_size"])[0] == v)
+            ref_lp = float(np.log(e[v] / e.sum()))
+            assert abs(lp[b, t - T0] - ref_lp) <= lp_tol, (b, t, lp[b, t - T0], ref_lp)
+            zl = z_lib[b, t - 1, :p["vocab_size"]]
+            el = np.exp(zl - zl.max())
+            assert abs(lp[b, t - T0] - float(np.log(el[v] / el.sum()))) <= lp_tol
+    say(f"[{be.name}] generate {preset}: {exact} of {B * (T - T0)} picks equal the oracle's")
+    # fp32: nearly every pick is the oracle's.  bf16: logit rounding moves
+    # cumulative boundaries by up to ~1e-3, and with 50257 near-uniform ids
+    # (intervals ~2e-5 wide) a fair share of picks may then differ; a wrong
+    # distribution would still match almost none.
+    assert exact >= (0.9 if preset == "fp32" else 0.5) * B * (T - T0)
+
+
 # ---------------------------------------------------------------------------- GPT-2 124M shapes
 
 def block_124m(be: Backend, B: int = 16, T: int = 1024):

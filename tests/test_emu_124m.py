@@ -54,3 +54,8 @@ def test_emu_full_batch_rows_and_determinism():
 @slow
 def test_emu_step_124m_one_sequence_all_layers():
     cases.step_124m_one_sequence(EMU, 64)
+
+
+@slow
+def test_emu_generate_124m_width():
+    cases.generate_matches_oracle(EMU, "124m", B=2, T0=8, T=14, n_layer=2)

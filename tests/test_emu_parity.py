@@ -112,3 +112,13 @@ def test_emu_checkpoint_resume_bitwise(preset):
 
 def test_emu_arena_guard_detects_overrun():
     cases.arena_guard_detects_overrun(EMU)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_emu_eval_loss_forward_only(preset):
+    cases.eval_loss_forward_only(EMU, preset)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_emu_generate_matches_oracle(preset):
+    cases.generate_matches_oracle(EMU, preset)

@@ -60,3 +60,13 @@ def test_checkpoint_resume_bitwise(preset):
 
 def test_arena_guard_detects_overrun():
     cases.arena_guard_detects_overrun(GPU)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_eval_loss_forward_only(preset):
+    cases.eval_loss_forward_only(GPU, preset)
+
+
+@pytest.mark.parametrize("preset", ["fp32", "bf16"])
+def test_generate_matches_oracle(preset):
+    cases.generate_matches_oracle(GPU, preset)

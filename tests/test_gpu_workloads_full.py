@@ -5,7 +5,9 @@
     B=4, T=1024;
   * the accumulated step's micro-batch shape B=32, T=512 with two real
     micro-steps at lr(132), and the full 32-micro-step accumulation against
-    the sum of the micro-steps' gradients.
+    the sum of the micro-steps' gradients;
+  * sampling with the key/value cache at the 124M shape (4 sequences, a
+    64-token prefix, 64 new tokens).
 The oracle takes each batch as one-sequence micro-batches (exactly the same
 step by linearity of accumulation, pinned on the CPU), so it never holds a
 whole batch's logits.  Each test stays well under pytest's 900 s limit on the
@@ -32,3 +34,7 @@ def test_accumulated_step_B32_T512_two_micro_steps():
 
 def test_accumulation_of_32_micro_steps_equals_their_sum():
     cases.accumulation_equals_sum_of_micro_steps(GPU, B=32, T=512, micro=32)
+
+
+def test_generate_124m_with_kv_cache():
+    cases.generate_matches_oracle(GPU, "124m", B=4, T0=64, T=128)

@@ -469,3 +469,81 @@ def test_bf16_rounding_of_inputs():
     r = inputs.round_to_bf16(a)
     t = torch.tensor(a).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(r, t)
+
+
+# ---------------------------------------------------------------------------- sampling
+
+def test_sample_token_is_the_inverse_cdf_by_brute_force():
+    """Against a pure-Python walk of the cumulative probabilities (math.exp,
+    running sum), for random logits and draws, padding ids excluded."""
+    import math as m
+    rng = np.random.default_rng(0)
+    for trial in range(200):
+        V = int(rng.integers(1, 12))
+        Vp = V + int(rng.integers(0, 4))
+        z = rng.standard_normal(Vp) * 3
+        z[V:] = 50.0  # padding logits are never tokens, however large
+        u = float(rng.random())
+        mx = max(z[:V])
+        e = [m.exp(float(x) - mx) for x in z[:V]]
+        S = sum(e)
+        run, want = 0.0, V - 1
+        for v in range(V):
+            run += e[v] / S
+            if run > u:
+                want = v
+                break
+        got, lp = O.sample_token(z, u, V)
+        assert got == want, (trial, got, want)
+        assert lp == pytest.approx(float(z[got]) - mx - m.log(S), abs=1e-12)
+
+
+def test_sample_token_frequencies_on_a_uniform_grid():
+    """With the draws on the grid (i + 1/2)/N, the share of each token is its
+    softmax probability within 1/N (the inverse CDF maps the grid onto the
+    probability intervals)."""
+    z = np.array([0.3, -1.2, 2.0, 0.0, 0.7, -0.4, 1.1])
+    N = 20000
+    counts = np.zeros(7)
+    for i in range(N):
+        counts[O.sample_token(z, (i + 0.5) / N, 7)[0]] += 1
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    assert np.all(np.abs(counts / N - p) <= 1.0 / N + 1e-12)
+    assert O.sample_token(z, 0.0, 7)[0] == 0 and O.sample_token(z, 1.0 - 1e-12, 7)[0] == 6
+
+
+def test_generate_agrees_with_one_forward_over_its_output():
+    """Teacher forcing: one forward over the generated sequence gives, at
+    every position t-1 >= T0-1, logits whose inverse-CDF sample at the
+    step's draw is token t and whose log-softmax at token t is the reported
+    log-probability (causality makes the step-by-step and the one-pass
+    logits equal).  The prefix is unchanged."""
+    cfg = TINY
+    P = _f64(O.init_params(cfg, 0))
+    rng = np.random.default_rng(4)
+    B, T0, T = 2, 5, 14
+    tok = np.zeros((B, T), np.int64)
+    tok[:, :T0] = rng.integers(0, cfg.vocab_size, (B, T0))
+    u = rng.random((B, T - T0))
+    out, lp = O.generate(P, tok, T0, u, cfg)
+    assert np.array_equal(out[:, :T0], tok[:, :T0])
+    _, _, cache = O.forward(P, out, None, cfg)
+    z = cache["z"].reshape(B, T, -1)
+    for b in range(B):
+        for t in range(T0, T):
+            v, l = O.sample_token(z[b, t - 1], u[b, t - T0], cfg.vocab_size)
+            assert v == out[b, t], (b, t)
+            assert l == pytest.approx(lp[b, t - T0], abs=1e-12)
+
+
+def test_eval_loss_is_the_forward_loss():
+    cfg = TINY
+    P = _f64(O.init_params(cfg, 0))
+    x, y = inputs.batch_from_stream(inputs.uniform_stream(1, 2 * 16 + 1, 512), 2, 16)
+    loss, per, _ = O.forward(P, x, y, cfg)
+    assert O.eval_loss(P, x, y, cfg) == loss
+    z = O.forward(P, x, None, cfg)[2]["z"]
+    zz = z - z.max(axis=1, keepdims=True)
+    ref = np.log(np.exp(zz).sum(1)) - zz[np.arange(32), y.reshape(-1)]
+    assert ref.mean() == pytest.approx(loss, rel=1e-13)
