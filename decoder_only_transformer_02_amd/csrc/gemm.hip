@@ -816,6 +816,132 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GP p) {
     for (int j = 0; j < 4; ++j) epi_store<EPI, float>(p, m0 + tr + i, n0 + tc + j, acc[i][j]);
 }
 
+// ------------------------------------------------------------------ fp32 MFMA kernel
+// fp32 operands on the matrix cores (v_mfma_f32_32x32x2_f32: 32x32 outputs,
+// 2 k per instruction, full fp32 products and sums): 128 x 128 block tiles,
+// 4 waves of 64 x 64 (2 x 2 fragments), K in stages of 16 through a
+// double-buffered LDS tile stored k-major ([k][row], rows padded to 160
+// floats so the two half-waves of a fragment read fall on disjoint banks).
+// Lane l supplies A[row l%32][k l/32] and B[k l/32][col l%32]; element e of
+// the accumulator is row 8(e/4) + 4(l/32) + e%4, column l%32.  Global loads
+// are 16 bytes along whichever of (row, k) is contiguous in memory and go
+// through registers, so the next stage's loads overlap the current MFMAs.
+// With blockIdx.z > 0 (split-K) each split covers p.kchunk of K.
+constexpr int F32M_BM = 128, F32M_BK = 16, F32M_LD = 160;
+
+template <bool TRANS>
+struct F32Loader {
+  // 128 rows x 16 k = 512 float4 per operand tile, 2 per thread.
+  float4 r[2];
+  __device__ __forceinline__ void load(const float* __restrict__ base, long ld, int row0, int nrows, int k0,
+                                       int kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      int row, k;
+      if constexpr (TRANS) {  // memory [k][row]: 4 consecutive rows
+        k = c >> 5;
+        row = (c & 31) * 4;
+      } else {                // memory [row][k]: 4 consecutive k
+        row = c >> 2;
+        k = (c & 3) * 4;
+      }
+      const int gr = row0 + row, gk = k0 + k;
+      const bool whole = TRANS ? (gr + 3 < nrows && gk < kend) : (gr < nrows && gk + 3 < kend);
+      if (whole && (ld & 3) == 0) {  // 16-byte aligned: row0, k0, row, k are multiples of 4
+        r[i] = TRANS ? *(const float4*)(base + (size_t)gk * ld + gr) : *(const float4*)(base + (size_t)gr * ld + gk);
+        continue;
+      }
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = TRANS ? gr + j : gr, kk = TRANS ? gk : gk + j;
+        v[j] = (rr < nrows && kk < kend) ? (TRANS ? base[(size_t)kk * ld + rr] : base[(size_t)rr * ld + kk])
+                                         : 0.f;
+      }
+      r[i] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __device__ __forceinline__ void store(float* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      if constexpr (TRANS) {
+        const int k = c >> 5, row = (c & 31) * 4;
+        *(float4*)(lds + k * F32M_LD + row) = r[i];
+      } else {
+        const int row = c >> 2, k = (c & 3) * 4;
+        lds[(k + 0) * F32M_LD + row] = r[i].x;
+        lds[(k + 1) * F32M_LD + row] = r[i].y;
+        lds[(k + 2) * F32M_LD + row] = r[i].z;
+        lds[(k + 3) * F32M_LD + row] = r[i].w;
+      }
+    }
+  }
+};
+
+template <bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_f32m(GP p) {
+  __shared__ float As[2][F32M_BK * F32M_LD], Bs[2][F32M_BK * F32M_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m0 = blockIdx.y * F32M_BM, n0 = blockIdx.x * F32M_BM;
+  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int kbeg = blockIdx.z * p.kchunk;
+  const int kend = min(p.K, kbeg + p.kchunk);
+  const int nk = kend > kbeg ? cdiv(kend - kbeg, F32M_BK) : 0;
+  const float* A = (const float*)p.A;
+  const float* B = (const float*)p.B;
+  F32Loader<AT> la;
+  F32Loader<BT> lb;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  if (nk > 0) {
+    la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
+    lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
+    la.store(As[0], tid);
+    lb.store(Bs[0], tid);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool nxt = kt + 1 < nk;
+    if (nxt) {
+      la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * F32M_BK, kend, tid);
+      lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * F32M_BK, kend, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < F32M_BK; ks += 2) {
+      const float* ar = As[cur] + (ks + fk) * F32M_LD;
+      const float* br = Bs[cur] + (ks + fk) * F32M_LD;
+      const float a0 = ar[wm + fr], a1 = ar[wm + 32 + fr];
+      const float b0 = br[wn + fr], b1 = br[wn + 32 + fr];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    if (nxt) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        epi_store<EPI, float>(p, m0 + wm + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3), n0 + wn + j * 32 + fr,
+                              acc[i][j][e]);
+}
+
 // ------------------------------------------------------------------ split-K reduction
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int S,
                                                        size_t n, float* out, float alpha,
@@ -1004,8 +1130,28 @@ static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// fp32 problems of 2^27 multiply-adds or more go to the matrix cores; the
+// small ones (the tiny model) keep the FMA kernel.  Weight gradients split K
+// (the tokens) so that the grid covers the 256 CUs, summed by the same
+// fixed-order reduction as the bf16 path.
 template <bool AT, bool BT, int EPI>
 static hipError_t launch_f32(const GemmArgs& a, GP p, hipStream_t st) {
+  if ((double)a.M * a.N * a.K >= 134217728.0) {
+    const int tiles = cdiv(a.M, F32M_BM) * cdiv(a.N, F32M_BM);
+    int S = 1;
+    if (EPI == EPI_WGRAD && a.ldo == a.N && a.splitk_ws && a.N % 4 == 0) {
+      S = min(16, max(1, 256 / tiles));
+      while (S > 1 && (size_t)S * a.M * a.N > a.splitk_ws_elems) --S;
+    }
+    p.kchunk = cdiv(cdiv(a.K, S), F32M_BK) * F32M_BK;
+    S = cdiv(a.K, p.kchunk);
+    GP q = p;
+    if (S > 1) q.out = a.splitk_ws;
+    k_gemm_f32m<AT, BT, EPI><<<dim3(cdiv(a.N, F32M_BM), cdiv(a.M, F32M_BM), S), 256, 0, st>>>(q);
+    if (S > 1)
+      k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, S, (size_t)a.M * a.N, (float*)a.out, a.alpha, a.beta);
+    return hipGetLastError();
+  }
   p.kchunk = a.K;
   k_gemm_f32<AT, BT, EPI><<<dim3(cdiv(a.N, 64), cdiv(a.M, 64), 1), 256, 0, st>>>(p);
   return hipGetLastError();

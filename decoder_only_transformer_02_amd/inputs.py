@@ -30,6 +30,9 @@ PRESETS = {
     "gpt2_124m_v50257": dict(n_layer=12, n_head=12, n_embd=768, block_size=1024,
                              vocab_size=50257, padded_vocab=50257, B=16, T=1024,
                              compute="bf16", tokens="zipf"),
+    # the same step in fp32 throughout (matrix-core fp32 GEMMs)
+    "gpt2_124m_fp32": dict(n_layer=12, n_head=12, n_embd=768, block_size=1024, vocab_size=50257,
+                           padded_vocab=50304, B=16, T=1024, compute="fp32", tokens="zipf"),
     # accumulated optimizer step: 32 micro-steps of B=32, T=512
     "gpt2_124m_accum": dict(n_layer=12, n_head=12, n_embd=768, block_size=1024,
                             vocab_size=50257, padded_vocab=50304, B=32, T=512, accum=32,

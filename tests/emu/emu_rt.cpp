@@ -398,6 +398,41 @@ f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return o;
 }
 
+namespace {
+struct MfmaF32In {
+  float a, b;
+  f32x16_t c;
+};
+void mfma_f32_fn(void*) {
+  float A[32][2], B[2][32], D[32][32];
+  for (int l = 0; l < 64; ++l) {
+    const MfmaF32In* p = (const MfmaF32In*)lane_in(l);
+    A[l & 31][l >> 5] = p ? p->a : 0.f;
+    B[l >> 5][l & 31] = p ? p->b : 0.f;
+    for (int e = 0; e < 16; ++e) D[8 * (e >> 2) + 4 * (l >> 5) + (e & 3)][l & 31] = p ? p->c[e] : 0.f;
+  }
+  for (int i = 0; i < 32; ++i)
+    for (int k = 0; k < 2; ++k)
+      for (int j = 0; j < 32; ++j) D[i][j] = std::fma(A[i][k], B[k][j], D[i][j]);
+  for (int l = 0; l < 64; ++l) {
+    f32x16_t o;
+    for (int e = 0; e < 16; ++e) o[e] = D[8 * (e >> 2) + 4 * (l >> 5) + (e & 3)][l & 31];
+    std::memcpy(lane_out(l), &o, sizeof(o));
+  }
+}
+}  // namespace
+
+f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c) {
+  MfmaF32In in;
+  in.a = a;
+  in.b = b;
+  in.c = c;
+  void* r = wave_collective(5, &in, sizeof(in), mfma_f32_fn, nullptr);
+  f32x16_t o;
+  std::memcpy(&o, r, sizeof(o));
+  return o;
+}
+
 // ------------------------------------------------------------------ LDS transpose read
 namespace {
 void tr_fn(void*) {

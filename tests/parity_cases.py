@@ -26,6 +26,7 @@ SMALL_FP32 = dict(n_layer=2, n_head=4, n_embd=64, block_size=64, vocab_size=301,
 G124 = inputs.PRESETS["gpt2_124m"]
 G124U = inputs.PRESETS["gpt2_124m_v50257"]
 G124A = inputs.PRESETS["gpt2_124m_accum"]
+G124F = inputs.PRESETS["gpt2_124m_fp32"]
 
 
 # ---------------------------------------------------------------------------- small configurations
@@ -386,6 +387,39 @@ def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6
     ref = O.train_step(oracle_init(oc, 0), _one_sequence_batches(x, y), oc, lr=lr, clip=1.0, t=1,
                        dt=np.float32)
     assert_bf16(loss, norm, gg, pp, ref, lr=lr)
+
+
+def full_step_fp32_vs_oracle(be: Backend, B: int, T: int, n_layer=None):
+    """The whole step in fp32 throughout at the 124M width (the GEMMs on the
+    fp32 matrix cores from 2^27 multiply-adds up): loss and norm within
+    1e-4 relative, every gradient within 1e-4 relative L2, and the
+    post-AdamW rule with 1e-3 where the gradients agree in sign (at 124M
+    some near-zero gradients may differ in sign even in fp32; they must be
+    under 0.1 % of the elements)."""
+    over = {} if n_layer is None else {"n_layer": n_layer}
+    lc, oc, p = configs(G124F, B, T, **over)
+    x, y = inputs.batch_from_stream(stream_for(p, B * T + 1, 0), B, T)
+    say(f"[{be.name}] fp32 full step layers={p['n_layer']} B={B} T={T}")
+    m = be.make(lc, 0)
+    loss = m.forward(be.dev(x), be.dev(y))
+    m.backward(1.0)
+    names = m.param_names()
+    norm = m.step(6e-4, 1.0)
+    gg = gpu_grads(m, names)
+    pp = gpu_params(m, names)
+    m.check_arena()
+    m.close()
+    ref = O.train_step(oracle_init(oc, 0), _one_sequence_batches(x, y), oc, lr=6e-4, clip=1.0, t=1,
+                       dt=np.float32)
+    say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
+    assert abs(loss - ref["loss"]) <= 1e-4 * ref["loss"]
+    assert abs(norm - ref["norm"]) <= 1e-4 * ref["norm"]
+    worst = max((rel_l2(gg[n], ref["grads"][n]), n) for n in ref["grads"])
+    say("worst gradient relative L2", worst)
+    assert worst[0] <= 1e-4, worst
+    flips = check_post_adamw(pp, ref["params"], gg, ref["grads"], 6e-4, exact=False)
+    say("sign-disagreement fraction", flips)
+    assert flips < 1e-3
 
 
 def accumulated_step_vs_oracle(be: Backend, B: int = 32, T: int = 512, micro: int = 2, n_layer=None):

@@ -59,3 +59,8 @@ def test_emu_step_124m_one_sequence_all_layers():
 @slow
 def test_emu_generate_124m_width():
     cases.generate_matches_oracle(EMU, "124m", B=2, T0=8, T=14, n_layer=2)
+
+
+@slow
+def test_emu_full_step_fp32_124m_width():
+    cases.full_step_fp32_vs_oracle(EMU, 2, 64, n_layer=2)

@@ -260,3 +260,49 @@ def test_emu_flash_attention_forward_backward(L, B, T, H):
         cos = float((g * r).sum() / np.sqrt((g * g).sum() * (r * r).sum()))
         assert cos >= 0.9999, (name, cos)
         close(g, r, 2 ** -5, name)
+
+
+# ---------------------------------------------------------------------------- fp32 matrix-core GEMMs
+
+@pytest.mark.parametrize("M,N,K,at,bt,epi", [
+    (520, 300, 1000, 0, 0, EPI_STORE),    # forward layout, ragged rows, columns and K
+    (517, 384, 700, 0, 0, EPI_GELU),
+    (640, 256, 1024, 0, 0, EPI_RESID),
+    (600, 320, 768, 0, 1, EPI_DGELU),     # dX layout (B transposed in memory)
+    (768, 768, 4096, 1, 1, EPI_WGRAD),    # weight gradient: 7 K splits + reduction
+    (300, 452, 1100, 1, 1, EPI_WGRAD),    # ragged weight gradient, accumulate
+])
+def test_emu_fp32_mfma_gemm(L, M, N, K, at, bt, epi):
+    """fp32 problems of 2^27 multiply-adds or more run on the fp32 matrix
+    cores; full fp32 products, so agreement with a float64 product is within
+    fp32 accumulation error."""
+    assert M * N * K >= 2 ** 27
+    rng = np.random.default_rng(M + N + K)
+    A = (rng.standard_normal((K, M)) if at else rng.standard_normal((M, K))).astype(np.float32)
+    B = (rng.standard_normal((K, N)) if bt else rng.standard_normal((N, K))).astype(np.float32) * 0.1
+    bias = rng.standard_normal(N).astype(np.float32)
+    aux = rng.standard_normal((M, N)).astype(np.float32)
+    out0 = rng.standard_normal((M, N)).astype(np.float32)
+    out = out0.copy()
+    out2 = np.zeros((M, N), np.float32)
+    alpha, beta = (0.5, 1.0) if (epi == EPI_WGRAD and M == 300) else (1.0, 0.0)
+    ws_n = L.emu_gemm_splitk_ws_elems(M, N, 16384)
+    ws = np.zeros(max(ws_n, 1), np.float32)
+    st = L.emu_gemm(M, N, K, ptr(A), M if at else K, at, ptr(B), N if bt else K, bt, epi, ptr(out), N,
+                    ptr(out2), ptr(aux), ptr(bias), alpha, beta, 0, ptr(ws), ws_n)
+    assert st == 0
+    a64 = A.astype(np.float64).T if at else A.astype(np.float64)
+    b64 = B.astype(np.float64) if bt else B.astype(np.float64).T
+    acc = a64 @ b64
+    b = bias.astype(np.float64)
+    if epi == EPI_STORE:
+        close(out, acc + b, 1e-5, "store")
+    elif epi == EPI_GELU:
+        close(out, acc + b, 1e-5, "u")
+        close(out2, O.gelu_tanh(acc + b), 1e-5, "gelu")
+    elif epi == EPI_RESID:
+        close(out, aux + acc + b, 1e-5, "residual")
+    elif epi == EPI_DGELU:
+        close(out, acc * O.gelu_tanh_grad(aux.astype(np.float64)), 1e-5, "gelu derivative")
+    else:
+        close(out, alpha * acc + beta * out0, 1e-5, "weight gradient")

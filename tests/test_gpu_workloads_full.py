@@ -7,7 +7,8 @@
     micro-steps at lr(132), and the full 32-micro-step accumulation against
     the sum of the micro-steps' gradients;
   * sampling with the key/value cache at the 124M shape (4 sequences, a
-    64-token prefix, 64 new tokens).
+    64-token prefix, 64 new tokens);
+  * the whole step in fp32 throughout (fp32 matrix-core GEMMs), B=4, T=1024.
 The oracle takes each batch as one-sequence micro-batches (exactly the same
 step by linearity of accumulation, pinned on the CPU), so it never holds a
 whole batch's logits.  Each test stays well under pytest's 900 s limit on the
@@ -38,3 +39,7 @@ def test_accumulation_of_32_micro_steps_equals_their_sum():
 
 def test_generate_124m_with_kv_cache():
     cases.generate_matches_oracle(GPU, "124m", B=4, T0=64, T=128)
+
+
+def test_full_step_fp32_124m():
+    cases.full_step_fp32_vs_oracle(GPU, 4, 1024)
