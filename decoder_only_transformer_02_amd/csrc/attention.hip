@@ -4,7 +4,8 @@
 // attention").  softmax(q k^T / sqrt(hd)) v with query i attending keys
 // j <= i.  q, k, v are read in place from the packed qkv rows [B*T, 3C].
 //
-// head_dim 64, bf16: matrix-core kernels.  Each wave owns 32 queries (or
+// head_dim 64, 16-bit operands (bf16 or fp16): matrix-core kernels.  Each
+// wave owns 32 queries (or
 // 32 keys in the dK/dV kernel) as the 32-wide MFMA column; K/V (or Q/dO)
 // tiles of 64 rows are staged in LDS and shared by the 4 waves of a block.
 // Scores are formed transposed (S^T = K Q^T) so that a lane holds 16 scores
@@ -22,28 +23,30 @@
 namespace gk {
 
 constexpr float LOG2E_F = 1.4426950408889634f;
-constexpr int ALD = 72;  // padded LDS row (bf16 elements)
+constexpr int ALD = 72;  // padded LDS row (16-bit elements)
 
-__device__ __forceinline__ uint4 ldg16(const bf16* p) { return *(const uint4*)p; }
+template <typename TE>
+__device__ __forceinline__ uint4 ldg16(const TE* p) { return *(const uint4*)p; }
 
-// 8 bf16 for the MFMA operand slots s = 0..7 gathered as keys
+// 8 values for the MFMA operand slots s = 0..7 gathered as keys
 // base + {0,1,2,3} and base + 8 + {0,1,2,3} from an LDS row (two 8-byte reads).
-__device__ __forceinline__ bf16x8 lds_two_runs(const uint16_t* row, int base) {
+template <typename TE>
+__device__ __forceinline__ typename H16<TE>::v8 lds_two_runs(const uint16_t* row, int base) {
   uint2 a = *(const uint2*)(row + base);
   uint2 b = *(const uint2*)(row + base + 8);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+  return __builtin_bit_cast(typename H16<TE>::v8, make_uint4(a.x, a.y, b.x, b.y));
 }
 
-// Pack accumulator values e = 8h .. 8h+7 of one 32x32 block to bf16 slots.
-__device__ __forceinline__ bf16x8 pack_slots(const f32x16& v, int h) {
-  uint4 u = make_uint4(pack_bf2(v[8 * h + 0], v[8 * h + 1]), pack_bf2(v[8 * h + 2], v[8 * h + 3]),
-                       pack_bf2(v[8 * h + 4], v[8 * h + 5]), pack_bf2(v[8 * h + 6], v[8 * h + 7]));
-  return __builtin_bit_cast(bf16x8, u);
+// Pack accumulator values e = 8h .. 8h+7 of one 32x32 block to 16-bit slots.
+template <typename TE>
+__device__ __forceinline__ typename H16<TE>::v8 pack_slots(const f32x16& v, int h) {
+  uint4 u = make_uint4(H16<TE>::pack2(v[8 * h + 0], v[8 * h + 1]), H16<TE>::pack2(v[8 * h + 2], v[8 * h + 3]),
+                       H16<TE>::pack2(v[8 * h + 4], v[8 * h + 5]), H16<TE>::pack2(v[8 * h + 6], v[8 * h + 7]));
+  return __builtin_bit_cast(typename H16<TE>::v8, u);
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) { return H16<bf16>::mfma(a, b, c); }
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) { return H16<f16>::mfma(a, b, c); }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -52,12 +55,13 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// A 64-row x 64-column bf16 tile held in registers between its global load
+// A 64-row x 64-column 16-bit tile held in registers between its global load
 // and its LDS store (2 x 16 bytes per thread), so the next tile's loads are
 // in flight while the current one is being consumed.  Rows >= T load as 0.
 struct Tile64 {
   uint4 v[2];
-  __device__ __forceinline__ void load(const bf16* base, int ld, int r0, int T) {
+  template <typename TE>
+  __device__ __forceinline__ void load(const TE* base, int ld, int r0, int T) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int c = threadIdx.x + i * 256;
@@ -90,9 +94,11 @@ struct Tile64 {
 };
 
 // ------------------------------------------------------------------ forward, hd = 64
-__global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv,
-                                                    bf16* __restrict__ out, float* __restrict__ lse,
+template <typename TE>
+__global__ __launch_bounds__(256) void k_attn_fwd64(const TE* __restrict__ qkv,
+                                                    TE* __restrict__ out, float* __restrict__ lse,
                                                     int T, int H, float sl2) {
+  typedef typename H16<TE>::v8 v8;
   __shared__ uint16_t Ks[64 * ALD];
   __shared__ uint16_t Vt[64 * ALD];
   const int C = H * 64, ld = 3 * C;
@@ -101,15 +107,15 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, g = lane >> 5;
   const int q = q0 + 32 * w + fr;
-  const bf16* base = qkv + (size_t)b * T * ld;
-  const bf16* kbase_p = base + C + h * 64;
-  const bf16* vbase_p = base + 2 * C + h * 64;
+  const TE* base = qkv + (size_t)b * T * ld;
+  const TE* kbase_p = base + C + h * 64;
+  const TE* vbase_p = base + 2 * C + h * 64;
 
-  bf16x8 qf[4];
+  v8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = __builtin_bit_cast(
-        bf16x8, q < T ? ldg16(base + (size_t)q * ld + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+        v8, q < T ? ldg16(base + (size_t)q * ld + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
 
   f32x16 oacc[2] = {zero16(), zero16()};
   float m_i = -INFINITY, l_i = 0.f;
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
+        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
         s[kb] = mfma(a, qf[ks], s[kb]);
       }
     const bool diag = k0 + 63 > q0 + 32 * w;  // tile reaches past the wave's first query
@@ -173,11 +179,11 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
       for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 pb = pack_slots(s[j >> 1], j & 1);
+      v8 pb = pack_slots<TE>(s[j >> 1], j & 1);
       int kbase = (j >> 1) * 32 + (j & 1) * 16 + g * 4;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        bf16x8 a = lds_two_runs(Vt + (db * 32 + fr) * ALD, kbase);
+        v8 a = lds_two_runs<TE>(Vt + (db * 32 + fr) * ALD, kbase);
         oacc[db] = mfma(a, pb, oacc[db]);
       }
     }
@@ -185,14 +191,14 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const bf16* __restrict__ qkv
   const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
   const float inv = 1.0f / l_tot;
   if (q < T) {
-    bf16* orow = out + ((size_t)b * T + q) * C + h * 64;
+    TE* orow = out + ((size_t)b * T + q) * C + h * 64;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         int d = db * 32 + e4 * 8 + g * 4;
-        *(uint2*)(orow + d) = make_uint2(pack_bf2(oacc[db][e4 * 4 + 0] * inv, oacc[db][e4 * 4 + 1] * inv),
-                                         pack_bf2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv));
+        *(uint2*)(orow + d) = make_uint2(H16<TE>::pack2(oacc[db][e4 * 4 + 0] * inv, oacc[db][e4 * 4 + 1] * inv),
+                                         H16<TE>::pack2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv));
       }
     if (g == 0) lse[(size_t)bh * T + q] = m_i + __log2f(l_tot);
   }
@@ -210,6 +216,15 @@ __device__ __forceinline__ float dot16<bf16>(const uint4& a, const uint4& b) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     s += bfbits2f(x[j] & 0xffffu) * bfbits2f(y[j] & 0xffffu) + bfbits2f(x[j] >> 16) * bfbits2f(y[j] >> 16);
+  return s;
+}
+template <>
+__device__ __forceinline__ float dot16<f16>(const uint4& a, const uint4& b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    s += H16<f16>::lo(x[j]) * H16<f16>::lo(y[j]) + H16<f16>::hi(x[j]) * H16<f16>::hi(y[j]);
   return s;
 }
 template <>
@@ -236,12 +251,14 @@ __global__ __launch_bounds__(256) void k_attn_bwd_pre(const TA* __restrict__ o,
 }
 
 // ------------------------------------------------------------------ dQ, hd = 64
-__global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
-                                                   const bf16* __restrict__ dout,
+template <typename TE>
+__global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
+                                                   const TE* __restrict__ dout,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ Dv,
-                                                   bf16* __restrict__ dqkv, int T, int H, float sl2,
+                                                   TE* __restrict__ dqkv, int T, int H, float sl2,
                                                    float scale) {
+  typedef typename H16<TE>::v8 v8;
   __shared__ uint16_t Ks[64 * ALD];
   __shared__ uint16_t Kt[64 * ALD];
   __shared__ uint16_t Vs[64 * ALD];
@@ -251,18 +268,18 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, g = lane >> 5;
   const int q = q0 + 32 * w + fr;
-  const bf16* base = qkv + (size_t)b * T * ld;
-  const bf16* dob = dout + (size_t)b * T * C;
-  const bf16* kp = base + C + h * 64;
-  const bf16* vp = base + 2 * C + h * 64;
+  const TE* base = qkv + (size_t)b * T * ld;
+  const TE* dob = dout + (size_t)b * T * C;
+  const TE* kp = base + C + h * 64;
+  const TE* vp = base + 2 * C + h * 64;
 
-  bf16x8 qf[4], dof[4];
+  v8 qf[4], dof[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     qf[ks] = __builtin_bit_cast(
-        bf16x8, q < T ? ldg16(base + (size_t)q * ld + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+        v8, q < T ? ldg16(base + (size_t)q * ld + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
     dof[ks] = __builtin_bit_cast(
-        bf16x8, q < T ? ldg16(dob + (size_t)q * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+        v8, q < T ? ldg16(dob + (size_t)q * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
   }
   const float lq = q < T ? lse[(size_t)bh * T + q] : 0.f;
   const float Dq = q < T ? Dv[(size_t)bh * T + q] : 0.f;
@@ -292,9 +309,9 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
+        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
         s = mfma(a, qf[ks], s);
-        bf16x8 v = __builtin_bit_cast(bf16x8, *(const uint4*)(Vs + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
+        v8 v = __builtin_bit_cast(v8, *(const uint4*)(Vs + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
         dp = mfma(v, dof[ks], dp);
       }
 #pragma unroll
@@ -308,36 +325,38 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const bf16* __restrict__ qkv,
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 dsb = pack_slots(s, hh);
+        v8 dsb = pack_slots<TE>(s, hh);
         int kbase = kb * 32 + hh * 16 + g * 4;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          bf16x8 a = lds_two_runs(Kt + (db * 32 + fr) * ALD, kbase);
+          v8 a = lds_two_runs<TE>(Kt + (db * 32 + fr) * ALD, kbase);
           dq[db] = mfma(a, dsb, dq[db]);
         }
       }
     }
   }
   if (q < T) {
-    bf16* row = dqkv + ((size_t)b * T + q) * ld + h * 64;
+    TE* row = dqkv + ((size_t)b * T + q) * ld + h * 64;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         int d = db * 32 + e4 * 8 + g * 4;
-        *(uint2*)(row + d) = make_uint2(pack_bf2(dq[db][e4 * 4 + 0] * scale, dq[db][e4 * 4 + 1] * scale),
-                                        pack_bf2(dq[db][e4 * 4 + 2] * scale, dq[db][e4 * 4 + 3] * scale));
+        *(uint2*)(row + d) = make_uint2(H16<TE>::pack2(dq[db][e4 * 4 + 0] * scale, dq[db][e4 * 4 + 1] * scale),
+                                        H16<TE>::pack2(dq[db][e4 * 4 + 2] * scale, dq[db][e4 * 4 + 3] * scale));
       }
   }
 }
 
 // ------------------------------------------------------------------ dK, dV, hd = 64
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dkv64(const bf16* __restrict__ qkv,
-                                                    const bf16* __restrict__ dout,
+template <typename TE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dkv64(const TE* __restrict__ qkv,
+                                                    const TE* __restrict__ dout,
                                                     const float* __restrict__ lse,
                                                     const float* __restrict__ Dv,
-                                                    bf16* __restrict__ dqkv, int T, int H, float sl2,
+                                                    TE* __restrict__ dqkv, int T, int H, float sl2,
                                                     float scale) {
+  typedef typename H16<TE>::v8 v8;
   __shared__ uint16_t Qs[64 * ALD];
   __shared__ uint16_t Qt[64 * ALD];
   __shared__ uint16_t Os[64 * ALD];   // dO [q][d]
@@ -349,18 +368,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 31, g = lane >> 5;
   const int key = k0 + 32 * w + fr;
-  const bf16* base = qkv + (size_t)b * T * ld;
-  const bf16* dob = dout + (size_t)b * T * C;
-  const bf16* qp = base + h * 64;
-  const bf16* op = dob + h * 64;
+  const TE* base = qkv + (size_t)b * T * ld;
+  const TE* dob = dout + (size_t)b * T * C;
+  const TE* qp = base + h * 64;
+  const TE* op = dob + h * 64;
 
-  bf16x8 kf[4], vf[4];
+  v8 kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     kf[ks] = __builtin_bit_cast(
-        bf16x8, key < T ? ldg16(base + (size_t)key * ld + C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+        v8, key < T ? ldg16(base + (size_t)key * ld + C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
     vf[ks] = __builtin_bit_cast(
-        bf16x8, key < T ? ldg16(base + (size_t)key * ld + 2 * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+        v8, key < T ? ldg16(base + (size_t)key * ld + 2 * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
   }
   f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
   const int wk_lo = k0 + 32 * w;
@@ -400,9 +419,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(Qs + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
+        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Qs + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
         s = mfma(a, kf[ks], s);
-        bf16x8 o = __builtin_bit_cast(bf16x8, *(const uint4*)(Os + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
+        v8 o = __builtin_bit_cast(v8, *(const uint4*)(Os + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
         dp = mfma(o, vf[ks], dp);
       }
 #pragma unroll
@@ -425,31 +444,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pb = pack_slots(s, hh);
-        bf16x8 dsb = pack_slots(dp, hh);
+        v8 pb = pack_slots<TE>(s, hh);
+        v8 dsb = pack_slots<TE>(dp, hh);
         int qbase = qb * 32 + hh * 16 + g * 4;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          bf16x8 ao = lds_two_runs(Ot + (db * 32 + fr) * ALD, qbase);
+          v8 ao = lds_two_runs<TE>(Ot + (db * 32 + fr) * ALD, qbase);
           dv[db] = mfma(ao, pb, dv[db]);
-          bf16x8 aq = lds_two_runs(Qt + (db * 32 + fr) * ALD, qbase);
+          v8 aq = lds_two_runs<TE>(Qt + (db * 32 + fr) * ALD, qbase);
           dk[db] = mfma(aq, dsb, dk[db]);
         }
       }
     }
   }
   if (key < T) {
-    bf16* rk = dqkv + ((size_t)b * T + key) * ld + C + h * 64;
-    bf16* rv = rk + C;
+    TE* rk = dqkv + ((size_t)b * T + key) * ld + C + h * 64;
+    TE* rv = rk + C;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         int d = db * 32 + e4 * 8 + g * 4;
-        *(uint2*)(rk + d) = make_uint2(pack_bf2(dk[db][e4 * 4 + 0] * scale, dk[db][e4 * 4 + 1] * scale),
-                                       pack_bf2(dk[db][e4 * 4 + 2] * scale, dk[db][e4 * 4 + 3] * scale));
-        *(uint2*)(rv + d) = make_uint2(pack_bf2(dv[db][e4 * 4 + 0], dv[db][e4 * 4 + 1]),
-                                       pack_bf2(dv[db][e4 * 4 + 2], dv[db][e4 * 4 + 3]));
+        *(uint2*)(rk + d) = make_uint2(H16<TE>::pack2(dk[db][e4 * 4 + 0] * scale, dk[db][e4 * 4 + 1] * scale),
+                                       H16<TE>::pack2(dk[db][e4 * 4 + 2] * scale, dk[db][e4 * 4 + 3] * scale));
+        *(uint2*)(rv + d) = make_uint2(H16<TE>::pack2(dv[db][e4 * 4 + 0], dv[db][e4 * 4 + 1]),
+                                       H16<TE>::pack2(dv[db][e4 * 4 + 2], dv[db][e4 * 4 + 3]));
       }
   }
 }
@@ -555,54 +574,62 @@ __global__ __launch_bounds__(128) void k_attn_dkv_gen(const TA* __restrict__ qkv
 // ------------------------------------------------------------------ host side
 size_t attn_bwd_workspace(int B, int T, int H) { return (size_t)B * H * T; }
 
-hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int hd, bool bf,
-                    hipStream_t st) {
-  if (hd > 128) return hipErrorInvalidValue;
-  const float scale = 1.0f / sqrtf((float)hd);
-  const float sl2 = scale * LOG2E_F;
-  if (bf && hd == 64) {
+template <typename TE>
+static hipError_t attn_fwd_t(const void* qkv, void* o, float* lse, int B, int T, int H, int hd, float sl2,
+                             hipStream_t st) {
+  if (hd == 64) {
     dim3 grid(cdiv(T, 128), B * H);
-    k_attn_fwd64<<<grid, 256, 0, st>>>((const bf16*)qkv, (bf16*)o, lse, T, H, sl2);
-  } else if (bf) {
-    k_attn_fwd_gen<bf16, 128><<<cdiv((long)B * H * T, 128), 128, 0, st>>>(
-        (const bf16*)qkv, (bf16*)o, lse, B, T, H, hd, sl2);
+    k_attn_fwd64<TE><<<grid, 256, 0, st>>>((const TE*)qkv, (TE*)o, lse, T, H, sl2);
   } else {
-    k_attn_fwd_gen<float, 128><<<cdiv((long)B * H * T, 128), 128, 0, st>>>(
-        (const float*)qkv, (float*)o, lse, B, T, H, hd, sl2);
+    k_attn_fwd_gen<TE, 128><<<cdiv((long)B * H * T, 128), 128, 0, st>>>((const TE*)qkv, (TE*)o, lse, B, T, H,
+                                                                        hd, sl2);
   }
   return hipGetLastError();
 }
 
+hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int dt,
+                    hipStream_t st) {
+  if (hd > 128) return hipErrorInvalidValue;
+  const float scale = 1.0f / sqrtf((float)hd);
+  const float sl2 = scale * LOG2E_F;
+  if (dt == ACT_BF16) return attn_fwd_t<bf16>(qkv, o, lse, B, T, H, hd, sl2, st);
+  if (dt == ACT_F16) return attn_fwd_t<f16>(qkv, o, lse, B, T, H, hd, sl2, st);
+  k_attn_fwd_gen<float, 128><<<cdiv((long)B * H * T, 128), 128, 0, st>>>(
+      (const float*)qkv, (float*)o, lse, B, T, H, hd, sl2);
+  return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t attn_bwd_t(const void* qkv, const void* o, const void* dout, const float* lse, void* dqkv,
+                             float* ws, int B, int T, int H, int hd, float sl2, float scale, hipStream_t st) {
+  const int n = B * T * H;
+  k_attn_bwd_pre<TA><<<cdiv(n, 256), 256, 0, st>>>((const TA*)o, (const TA*)dout, ws, B, T, H, hd);
+  if constexpr (sizeof(TA) == 2) {
+    if (hd == 64) {
+      dim3 grid(cdiv(T, 128), B * H);
+      k_attn_dq64<TA><<<grid, 256, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, T, H, sl2,
+                                            scale);
+      k_attn_dkv64<TA><<<grid, 256, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, T, H, sl2,
+                                             scale);
+      return hipGetLastError();
+    }
+  }
+  const int g = cdiv((long)B * H * T, 128);
+  k_attn_dq_gen<TA, 128><<<g, 128, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, B, T, H, hd,
+                                            sl2, scale);
+  k_attn_dkv_gen<TA, 128><<<g, 128, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, B, T, H, hd,
+                                             sl2, scale);
+  return hipGetLastError();
+}
+
 hipError_t attn_bwd(const void* qkv, const void* o, const void* dout, const float* lse, void* dqkv,
-                    float* ws, int B, int T, int H, int hd, bool bf, hipStream_t st) {
+                    float* ws, int B, int T, int H, int hd, int dt, hipStream_t st) {
   if (hd > 128 || hd % 8) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)hd);
   const float sl2 = scale * LOG2E_F;
-  int n = B * T * H;
-  if (bf)
-    k_attn_bwd_pre<bf16><<<cdiv(n, 256), 256, 0, st>>>((const bf16*)o, (const bf16*)dout, ws, B, T, H, hd);
-  else
-    k_attn_bwd_pre<float><<<cdiv(n, 256), 256, 0, st>>>((const float*)o, (const float*)dout, ws, B, T, H, hd);
-  if (bf && hd == 64) {
-    dim3 grid(cdiv(T, 128), B * H);
-    k_attn_dq64<<<grid, 256, 0, st>>>((const bf16*)qkv, (const bf16*)dout, lse, ws, (bf16*)dqkv, T,
-                                      H, sl2, scale);
-    k_attn_dkv64<<<grid, 256, 0, st>>>((const bf16*)qkv, (const bf16*)dout, lse, ws, (bf16*)dqkv, T,
-                                       H, sl2, scale);
-  } else if (bf) {
-    int g = cdiv((long)B * H * T, 128);
-    k_attn_dq_gen<bf16, 128><<<g, 128, 0, st>>>((const bf16*)qkv, (const bf16*)dout, lse, ws,
-                                                (bf16*)dqkv, B, T, H, hd, sl2, scale);
-    k_attn_dkv_gen<bf16, 128><<<g, 128, 0, st>>>((const bf16*)qkv, (const bf16*)dout, lse, ws,
-                                                 (bf16*)dqkv, B, T, H, hd, sl2, scale);
-  } else {
-    int g = cdiv((long)B * H * T, 128);
-    k_attn_dq_gen<float, 128><<<g, 128, 0, st>>>((const float*)qkv, (const float*)dout, lse, ws,
-                                                 (float*)dqkv, B, T, H, hd, sl2, scale);
-    k_attn_dkv_gen<float, 128><<<g, 128, 0, st>>>((const float*)qkv, (const float*)dout, lse, ws,
-                                                  (float*)dqkv, B, T, H, hd, sl2, scale);
-  }
-  return hipGetLastError();
+  if (dt == ACT_BF16) return attn_bwd_t<bf16>(qkv, o, dout, lse, dqkv, ws, B, T, H, hd, sl2, scale, st);
+  if (dt == ACT_F16) return attn_bwd_t<f16>(qkv, o, dout, lse, dqkv, ws, B, T, H, hd, sl2, scale, st);
+  return attn_bwd_t<float>(qkv, o, dout, lse, dqkv, ws, B, T, H, hd, sl2, scale, st);
 }
 
 }  // namespace gk

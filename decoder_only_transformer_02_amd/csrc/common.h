@@ -13,6 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define WAVE 64
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Round-to-nearest-even float -> bf16 (the gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f2bf_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -30,6 +33,10 @@ template <> struct Cvt<bf16> {
   }
   static __device__ __forceinline__ bf16 from_f(float x) { return (__bf16)x; }
 };
+template <> struct Cvt<f16> {
+  static __device__ __forceinline__ float to_f(f16 x) { return (float)x; }
+  static __device__ __forceinline__ f16 from_f(float x) { return (f16)x; }
+};
 template <typename T> __device__ __forceinline__ float to_f(T x) { return Cvt<T>::to_f(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return Cvt<T>::from_f(x); }
 
@@ -40,6 +47,35 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   v[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, v);
 }
+
+// The two 16-bit storage types of the matrix-core path, bf16 and fp16 (IEEE
+// half): the 8-element MFMA operand vector, the 32x32x16 matrix instruction
+// with fp32 accumulation, and packing of two floats into one dword (low
+// half = first, round to nearest even) and back.
+template <typename T> struct H16;
+template <> struct H16<bf16> {
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf2(a, b); }
+  static __device__ __forceinline__ float lo(uint32_t u) { return bfbits2f(u & 0xffffu); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return bfbits2f(u >> 16); }
+};
+template <> struct H16<f16> {
+  typedef f16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f16x2 v;
+    v[0] = (f16)a;
+    v[1] = (f16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float lo(uint32_t u) { return (float)__builtin_bit_cast(f16, (uint16_t)(u & 0xffffu)); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return (float)__builtin_bit_cast(f16, (uint16_t)(u >> 16)); }
+};
 
 // Wavefront (64 lanes) all-reduce.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -25,9 +25,9 @@ __global__ __launch_bounds__(256) void k_kv_store(const uint8_t* __restrict__ qk
   for (int k = threadIdx.x; k < chunks; k += 256) dst[k] = src[k];
 }
 
-hipError_t kv_store(const void* qkv, void* cache, int B, int n, int t0, int Tmax, int C, bool bf,
+hipError_t kv_store(const void* qkv, void* cache, int B, int n, int t0, int Tmax, int C, int dt,
                     hipStream_t st) {
-  const int es = bf ? 2 : 4;
+  const int es = dt == ACT_F32 ? 4 : 2;
   if ((2 * C * es) % 16 || B < 1 || n < 1 || t0 < 0 || t0 + n > Tmax) return hipErrorInvalidValue;
   k_kv_store<<<B * n, 256, 0, st>>>((const uint8_t*)qkv, (uint8_t*)cache, B, n, t0, Tmax, C, es);
   return hipGetLastError();
@@ -92,10 +92,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(const TA* __restrict__ qkv,
 }
 
 hipError_t attn_decode(const void* qkv, const void* cache, void* out, int B, int H, int hd, int Tmax, int nkeys,
-                       bool bf, hipStream_t st) {
+                       int dt, hipStream_t st) {
   if (hd > 128 || nkeys < 1 || nkeys > Tmax) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
-  if (bf)
+  if (dt == ACT_F16)
+    k_attn_decode<f16><<<B * H, 256, 0, st>>>((const f16*)qkv, (const f16*)cache, (f16*)out, H, hd, Tmax, nkeys,
+                                               sl2);
+  else if (dt == ACT_BF16)
     k_attn_decode<bf16><<<B * H, 256, 0, st>>>((const bf16*)qkv, (const bf16*)cache, (bf16*)out, H, hd, Tmax,
                                                 nkeys, sl2);
   else
@@ -176,10 +179,13 @@ __global__ __launch_bounds__(256) void k_sample(const TL* __restrict__ logits, i
   }
 }
 
-hipError_t sample(const void* logits, bool bf, int ld, int row_stride, int row0, int V, int B, const float* u,
+hipError_t sample(const void* logits, int dt, int ld, int row_stride, int row0, int V, int B, const float* u,
                   int u_stride, int32_t* tok, int tok_stride, float* logprob, int lp_stride, hipStream_t st) {
   if (B < 1 || V < 1 || V > ld) return hipErrorInvalidValue;
-  if (bf)
+  if (dt == ACT_F16)
+    k_sample<f16><<<B, 256, 0, st>>>((const f16*)logits, ld, row_stride, row0, V, u, u_stride, tok, tok_stride,
+                                      logprob, lp_stride);
+  else if (dt == ACT_BF16)
     k_sample<bf16><<<B, 256, 0, st>>>((const bf16*)logits, ld, row_stride, row0, V, u, u_stride, tok, tok_stride,
                                        logprob, lp_stride);
   else

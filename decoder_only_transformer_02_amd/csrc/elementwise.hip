@@ -28,9 +28,18 @@ template <> struct Vec4<bf16> {
     *(uint2*)p = make_uint2(pack_bf2(a, b), pack_bf2(c, d));
   }
 };
+template <> struct Vec4<f16> {
+  static __device__ __forceinline__ float4 load(const f16* p) {
+    uint2 u = *(const uint2*)p;
+    return make_float4(H16<f16>::lo(u.x), H16<f16>::hi(u.x), H16<f16>::lo(u.y), H16<f16>::hi(u.y));
+  }
+  static __device__ __forceinline__ void store(f16* p, float a, float b, float c, float d) {
+    *(uint2*)p = make_uint2(H16<f16>::pack2(a, b), H16<f16>::pack2(c, d));
+  }
+};
 
 // flag bits
-enum { FLAG_TOKEN = 1, FLAG_TARGET = 2, FLAG_LOSS = 4, FLAG_NORM = 8 };
+enum { FLAG_TOKEN = 1, FLAG_TARGET = 2, FLAG_LOSS = 4, FLAG_NORM = 8, FLAG_OVERFLOW = 16 };
 
 // ------------------------------------------------------------------ embedding forward
 // "From Scratch: Building GPT-2 ...", Key Features: token and positional
@@ -116,12 +125,14 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
   }
 }
 
-hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, bool y_bf16, float* mean,
+hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, int dt, float* mean,
                   float* rstd, int M, int C, float eps, hipStream_t st) {
   if (C % 4 || C > 1024) return hipErrorInvalidValue;
   int g = cdiv(M, 4);
-  if (y_bf16)
+  if (dt == ACT_BF16)
     k_ln_fwd<bf16, 4><<<g, 256, 0, st>>>(x, w, b, (bf16*)y, mean, rstd, M, C, eps);
+  else if (dt == ACT_F16)
+    k_ln_fwd<f16, 4><<<g, 256, 0, st>>>(x, w, b, (f16*)y, mean, rstd, M, C, eps);
   else
     k_ln_fwd<float, 4><<<g, 256, 0, st>>>(x, w, b, (float*)y, mean, rstd, M, C, eps);
   return hipGetLastError();
@@ -215,14 +226,17 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 }
 
 hipError_t ln_bwd(const float* x, const float* mean, const float* rstd, const float* w,
-                  const void* dy, bool act_bf16, float* dres, void* dres_act, bool accum,
+                  const void* dy, int dt, float* dres, void* dres_act, bool accum,
                   float* part, int M, int C, hipStream_t st) {
   if (C % 4 || C > 1024) return hipErrorInvalidValue;
   int nb = ln_bwd_blocks(M);
   int rpb = cdiv(M, nb);
-  if (act_bf16)
+  if (dt == ACT_BF16)
     k_ln_bwd<bf16, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const bf16*)dy, dres, (bf16*)dres_act,
                                           accum, part, M, C, rpb);
+  else if (dt == ACT_F16)
+    k_ln_bwd<f16, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const f16*)dy, dres, (f16*)dres_act,
+                                         accum, part, M, C, rpb);
   else
     k_ln_bwd<float, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const float*)dy, dres,
                                            (float*)dres_act, accum, part, M, C, rpb);
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(256) void k_colsum_part(const T* __restrict__ X, in
       if constexpr (E == 8) {
         uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[c8 + j] += bfbits2f((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+        for (int j = 0; j < 8; ++j) acc[c8 + j] += (j & 1) ? H16<T>::hi(w[j >> 1]) : H16<T>::lo(w[j >> 1]);
       } else {
         acc[c8 + 0] += __uint_as_float(u.x); acc[c8 + 1] += __uint_as_float(u.y);
         acc[c8 + 2] += __uint_as_float(u.z); acc[c8 + 3] += __uint_as_float(u.w);
@@ -329,14 +343,16 @@ __global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ 
   db[n] = (beta != 0.f ? beta * db[n] : 0.f) + s;
 }
 
-hipError_t colsum(const void* X, bool x_bf16, int M, int N, int ldx, float* db, float beta,
+hipError_t colsum(const void* X, int dt, int M, int N, int ldx, float* db, float beta,
                   float* part, hipStream_t st) {
   if (N % 8 || ldx % 8) return hipErrorInvalidValue;
   int R = colsum_parts(M);
   int rows_per = cdiv(M, R);
   dim3 g(cdiv(N, 256), R);
-  if (x_bf16)
+  if (dt == ACT_BF16)
     k_colsum_part<bf16><<<g, 256, 0, st>>>((const bf16*)X, M, N, ldx, rows_per, part);
+  else if (dt == ACT_F16)
+    k_colsum_part<f16><<<g, 256, 0, st>>>((const f16*)X, M, N, ldx, rows_per, part);
   else
     k_colsum_part<float><<<g, 256, 0, st>>>((const float*)X, M, N, ldx, rows_per, part);
   k_colsum_final<<<cdiv(N, 256), 256, 0, st>>>(part, R, N, db, beta);
@@ -382,6 +398,11 @@ __device__ __forceinline__ float chunk_elem<bf16>(const uint4& u, int j) {
   uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
   return bfbits2f((j & 1) ? (w >> 16) : (w & 0xffffu));
 }
+template <>
+__device__ __forceinline__ float chunk_elem<f16>(const uint4& u, int j) {
+  uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
+  return (j & 1) ? H16<f16>::hi(w) : H16<f16>::lo(w);
+}
 
 template <typename T>
 __device__ __forceinline__ uint4 chunk_pack(const float* f);
@@ -395,14 +416,21 @@ __device__ __forceinline__ uint4 chunk_pack<bf16>(const float* f) {
   return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]),
                     pack_bf2(f[6], f[7]));
 }
+template <>
+__device__ __forceinline__ uint4 chunk_pack<f16>(const float* f) {
+  return make_uint4(H16<f16>::pack2(f[0], f[1]), H16<f16>::pack2(f[2], f[3]), H16<f16>::pack2(f[4], f[5]),
+                    H16<f16>::pack2(f[6], f[7]));
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <typename T, int NCH>
+// DS: the gradient scale is also multiplied by *dev_scale (the dynamic
+// loss scale of the fp16 workload, which lives on the device).
+template <typename T, int NCH, bool DS>
 __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, int V, int vt,
                                               const int32_t* __restrict__ tgt,
                                               float* __restrict__ losses, float scale,
-                                              int want_grad, int* flag) {
+                                              int want_grad, int* flag, const float* dev_scale) {
   constexpr int E = Chunk16<T>::E;
   __shared__ float sh[4];
   int row = blockIdx.x;
@@ -447,6 +475,7 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
   float lse = mx + __logf(s);
   if (threadIdx.x == 0) losses[row] = lse - zy;
   if (!want_grad) return;
+  if constexpr (DS) scale *= dev_scale[0];
   float lse2 = lse * LOG2E;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
@@ -470,11 +499,11 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
 }
 
 // Streaming variant (row too long for registers): three passes over HBM.
-template <typename T>
+template <typename T, bool DS>
 __global__ __launch_bounds__(256) void k_xent_stream(T* __restrict__ logits, int ld, int V, int vt,
                                                      const int32_t* __restrict__ tgt,
                                                      float* __restrict__ losses, float scale,
-                                                     int want_grad, int* flag) {
+                                                     int want_grad, int* flag, const float* dev_scale) {
   __shared__ float sh[4];
   int row = blockIdx.x;
   T* z = logits + (size_t)row * ld;
@@ -499,6 +528,7 @@ __global__ __launch_bounds__(256) void k_xent_stream(T* __restrict__ logits, int
   float lse = mx + __logf(s);
   if (threadIdx.x == 0) losses[row] = lse - zy;
   if (!want_grad) return;
+  if constexpr (DS) scale *= dev_scale[0];
   __syncthreads();
   float lse2 = lse * LOG2E;
   for (int e = threadIdx.x; e < ld; e += 256) {
@@ -512,37 +542,44 @@ __global__ __launch_bounds__(256) void k_xent_stream(T* __restrict__ logits, int
   }
 }
 
-template <typename T>
+template <typename T, bool DS>
 static hipError_t xent_t(T* logits, int ld, int V, int vt, const int32_t* tgt, float* losses, float scale,
-                         bool want_grad, int M, int* flag, hipStream_t st) {
+                         bool want_grad, int M, int* flag, const float* ds, hipStream_t st) {
   constexpr int E = Chunk16<T>::E;
   int nch = cdiv(cdiv(ld, E), 256);
   int g = want_grad ? 1 : 0;
   if (nch <= 1)
-    k_xent<T, 1><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 1, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else if (nch <= 2)
-    k_xent<T, 2><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 2, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else if (nch <= 4)
-    k_xent<T, 4><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 4, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else if (nch <= 8)
-    k_xent<T, 8><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 8, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else if (nch <= 16)
-    k_xent<T, 16><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 16, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else if (nch <= 25)
-    k_xent<T, 25><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent<T, 25, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   else
-    k_xent_stream<T><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag);
+    k_xent_stream<T, DS><<<M, 256, 0, st>>>(logits, ld, V, vt, tgt, losses, scale, g, flag, ds);
   return hipGetLastError();
 }
 
-hipError_t xent(void* logits, bool bf16_logits, int ld, int V, int vt, const int32_t* tgt,
-                float* losses, float scale, bool want_grad, int M, int* flag, hipStream_t st) {
-  if (bf16_logits) {
+hipError_t xent(void* logits, int dt, int ld, int V, int vt, const int32_t* tgt, float* losses, float scale,
+                bool want_grad, int M, int* flag, const float* dev_scale, hipStream_t st) {
+  if (dt == ACT_F16) {
     if (ld % 8) return hipErrorInvalidValue;
-    return xent_t<bf16>((bf16*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, st);
+    if (dev_scale)
+      return xent_t<f16, true>((f16*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, dev_scale, st);
+    return xent_t<f16, false>((f16*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, nullptr, st);
+  }
+  if (dev_scale) return hipErrorInvalidValue;  // dynamic loss scaling is the fp16 workload's
+  if (dt == ACT_BF16) {
+    if (ld % 8) return hipErrorInvalidValue;
+    return xent_t<bf16, false>((bf16*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, nullptr, st);
   }
   if (ld % 4) return hipErrorInvalidValue;
-  return xent_t<float>((float*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, st);
+  return xent_t<float, false>((float*)logits, ld, V, vt, tgt, losses, scale, want_grad, M, flag, nullptr, st);
 }
 
 // mean loss, float64 accumulation in a fixed order
@@ -741,9 +778,17 @@ hipError_t sumsq(const float* g, size_t n, double* part, hipStream_t st) {
 
 // scal: [0] norm, [1] clip coefficient min(1, clip / (norm + 1e-6)),
 // [2] 1 - beta1^t, [3] 1 - beta2^t, [4] skip flag, [5] step count t.
+// LS (dynamic loss scaling, "Let's reproduce GPT-2 (124M)" chapter
+// "float16, gradient scalers"): the gradients carry the loss scale
+// S = scal[10]; the norm reported is theirs divided by S, and [1] becomes
+// the clip coefficient divided by S, so AdamW sees unscaled clipped
+// gradients.  A non-finite norm (an fp16 overflow) skips the update and
+// halves S; otherwise [11] counts the steps since the last change of S and
+// S doubles when it reaches growth_interval.
+template <bool LS>
 __global__ __launch_bounds__(256) void k_norm_finalize(const double* __restrict__ part, int nblk,
                                                        float clip, float beta1, float beta2,
-                                                       float* scal, int* flag) {
+                                                       float* scal, int* flag, int growth_interval) {
   __shared__ double sh[4];
   double s = 0.0;
   for (int i = threadIdx.x; i < nblk; i += 256) s += part[i];
@@ -752,26 +797,47 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const double* __restrict_
   __syncthreads();
   if (threadIdx.x == 0) {
     double nrm = sqrt((sh[0] + sh[1]) + (sh[2] + sh[3]));
+    const float S = LS ? scal[10] : 1.f;
+    if constexpr (LS) nrm /= (double)S;
     scal[0] = (float)nrm;
     if (isfinite(nrm)) {
       double c = (double)clip / (nrm + 1e-6);
-      scal[1] = (float)(c < 1.0 ? c : 1.0);
+      c = c < 1.0 ? c : 1.0;
+      scal[1] = LS ? (float)(c / (double)S) : (float)c;
       float t = scal[5] + 1.0f;
       scal[5] = t;
       scal[2] = (float)(1.0 - pow((double)beta1, (double)t));
       scal[3] = (float)(1.0 - pow((double)beta2, (double)t));
       scal[4] = 0.f;
+      if constexpr (LS) {
+        const float good = scal[11] + 1.f;
+        if (good >= (float)growth_interval) {
+          scal[10] = S * 2.f;
+          scal[11] = 0.f;
+        } else {
+          scal[11] = good;
+        }
+      }
     } else {
       scal[1] = 0.f;
       scal[4] = 1.f;
-      atomicOr(flag, FLAG_NORM);
+      if constexpr (LS) {
+        scal[10] = S * 0.5f;
+        scal[11] = 0.f;
+        atomicOr(flag, FLAG_OVERFLOW);
+      } else {
+        atomicOr(flag, FLAG_NORM);
+      }
     }
   }
 }
 
 hipError_t norm_finalize(const double* part, int nblk, float clip, float beta1, float beta2,
-                         float* scal, int* flag, hipStream_t st) {
-  k_norm_finalize<<<1, 256, 0, st>>>(part, nblk, clip, beta1, beta2, scal, flag);
+                         float* scal, int* flag, bool loss_scaling, int growth_interval, hipStream_t st) {
+  if (loss_scaling)
+    k_norm_finalize<true><<<1, 256, 0, st>>>(part, nblk, clip, beta1, beta2, scal, flag, growth_interval);
+  else
+    k_norm_finalize<false><<<1, 256, 0, st>>>(part, nblk, clip, beta1, beta2, scal, flag, growth_interval);
   return hipGetLastError();
 }
 
@@ -779,6 +845,7 @@ hipError_t norm_finalize(const double* part, int nblk, float clip, float beta1, 
 // "Optimization Hyperparameters": AdamW with betas (0.9, 0.95), eps 1e-8,
 // decoupled decay on 2-D tensors only; gradients pre-scaled by the clip
 // coefficient.  One block per table chunk; float4 vectorized.
+template <typename TS>
 __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const float* __restrict__ g,
                                                float* __restrict__ m, float* __restrict__ v,
                                                uint16_t* __restrict__ shadow,
@@ -808,14 +875,17 @@ __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const floa
     *(float4*)(p + i) = make_float4(pa[0], pa[1], pa[2], pa[3]);
     *(float4*)(m + i) = make_float4(ma[0], ma[1], ma[2], ma[3]);
     *(float4*)(v + i) = make_float4(va[0], va[1], va[2], va[3]);
-    if (wsh) *(uint2*)(shadow + i) = make_uint2(pack_bf2(pa[0], pa[1]), pack_bf2(pa[2], pa[3]));
+    if (wsh) *(uint2*)(shadow + i) = make_uint2(H16<TS>::pack2(pa[0], pa[1]), H16<TS>::pack2(pa[2], pa[3]));
   }
 }
 
-hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow,
+hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow, int shadow_dt,
                  const AdamChunk* chunks, int nchunks, const float* scal, float lr, float beta1,
                  float beta2, float eps, float wd, hipStream_t st) {
-  k_adamw<<<nchunks, 256, 0, st>>>(p, g, m, v, shadow, chunks, scal, lr, beta1, beta2, eps, wd);
+  if (shadow_dt == ACT_F16)
+    k_adamw<f16><<<nchunks, 256, 0, st>>>(p, g, m, v, shadow, chunks, scal, lr, beta1, beta2, eps, wd);
+  else
+    k_adamw<bf16><<<nchunks, 256, 0, st>>>(p, g, m, v, shadow, chunks, scal, lr, beta1, beta2, eps, wd);
   return hipGetLastError();
 }
 
@@ -859,8 +929,16 @@ __global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y,
        i += (size_t)gridDim.x * blockDim.x)
     y[i] = f2bf_bits(x[i]);
 }
-hipError_t to_bf16(const float* x, uint16_t* y, size_t n, hipStream_t st) {
-  k_to_bf16<<<2048, 256, 0, st>>>(x, y, n);
+__global__ void k_to_f16(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    y[i] = __builtin_bit_cast(uint16_t, (f16)x[i]);
+}
+hipError_t to_h16(const float* x, uint16_t* y, size_t n, int dt, hipStream_t st) {
+  if (dt == ACT_F16)
+    k_to_f16<<<2048, 256, 0, st>>>(x, y, n);
+  else
+    k_to_bf16<<<2048, 256, 0, st>>>(x, y, n);
   return hipGetLastError();
 }
 __global__ void k_fill(float* x, size_t n, float v) {
@@ -878,9 +956,11 @@ __global__ void k_copy_act(const float* __restrict__ x, T* __restrict__ y, size_
        i += (size_t)gridDim.x * blockDim.x)
     y[i] = from_f<T>(x[i]);
 }
-hipError_t copy_f32_to_act(const float* x, void* y, bool bf, size_t n, hipStream_t st) {
-  if (bf)
+hipError_t copy_f32_to_act(const float* x, void* y, int dt, size_t n, hipStream_t st) {
+  if (dt == ACT_BF16)
     k_copy_act<bf16><<<2048, 256, 0, st>>>(x, (bf16*)y, n);
+  else if (dt == ACT_F16)
+    k_copy_act<f16><<<2048, 256, 0, st>>>(x, (f16*)y, n);
   else
     k_copy_act<float><<<2048, 256, 0, st>>>(x, (float*)y, n);
   return hipGetLastError();

@@ -99,10 +99,11 @@ bool config_ok(const gpt2_config* c, std::string* why) {
   if (c->block_size < 1 || c->max_seq < 1 || c->max_seq > c->block_size) return bad("bad seq sizes");
   if (c->max_batch < 1 || (int64_t)c->max_batch * c->max_seq > 32768)
     return bad("max_batch * max_seq must be in [1, 32768]");
-  if (c->compute != GPT2_FP32 && c->compute != GPT2_BF16) return bad("bad compute mode");
+  if (c->compute != GPT2_FP32 && c->compute != GPT2_BF16 && c->compute != GPT2_FP16)
+    return bad("bad compute mode");
   // the GEMM operand loads address the logits with 32-bit byte offsets
   const uint64_t ldl = ((uint64_t)c->padded_vocab + 63) / 64 * 64;
-  if ((uint64_t)c->max_batch * c->max_seq * ldl * (c->compute == GPT2_BF16 ? 2u : 4u) >= (1ull << 32))
+  if ((uint64_t)c->max_batch * c->max_seq * ldl * (c->compute == GPT2_FP32 ? 4u : 2u) >= (1ull << 32))
     return bad("logits buffer of 4 GiB or more");
   return true;
 }
@@ -136,12 +137,16 @@ struct gpt2_ctx {
   size_t nflat = 0;          // flat array length (padded)
   size_t nflat_t = 0;        // transposed-copy array length
   int L, H, C, hd, V, Vp, ldl, maxM;
-  bool bf;
+  bool h16;     // 16-bit activations and GEMM operands (bf16 or fp16)
+  int dt;       // activation type (gk::ActType)
+  bool ls;      // dynamic loss scaling (fp16)
+  int ls_interval = 2000;
+  float ls_staging[2] = {0.f, 0.f};
   size_t act_es;  // activation element size
 
   float *params, *grads, *am, *av;
   uint16_t* shadow;
-  uint16_t* shadow_t;              // transposed bf16 copies of the GEMM weights
+  uint16_t* shadow_t;              // transposed 16-bit copies of the GEMM weights
   std::vector<size_t> toff;        // element offset of each transposed copy (or -1)
   std::vector<int> tld;            // its row stride
   std::vector<float*> h, mean, rstd, lse;
@@ -174,9 +179,9 @@ struct gpt2_ctx {
   const float* P(int j) const { return params + poff[j]; }
   float* G(int j) const { return grads + poff[j]; }
   const void* W(int j) const {  // GEMM operand copy of a weight
-    return bf ? (const void*)(shadow + poff[j]) : (const void*)(params + poff[j]);
+    return h16 ? (const void*)(shadow + poff[j]) : (const void*)(params + poff[j]);
   }
-  const void* Wt(int j) const { return shadow_t + toff[j]; }  // [in, out] (bf16 only)
+  const void* Wt(int j) const { return shadow_t + toff[j]; }  // [in, out] (16-bit only)
   int li(int l, int k) const { return 2 + 12 * l + k; }  // parameter index in layer l
   void* act(void* base, size_t elems_off) const { return (char*)base + elems_off * act_es; }
 };
@@ -229,8 +234,8 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   auto specs = param_specs(c);
   const int L = c.n_layer, C = c.n_embd, H = c.n_head;
   const int64_t maxM = (int64_t)c.max_batch * c.max_seq;
-  const bool bf = c.compute == GPT2_BF16;
-  const int adt = bf ? GPT2_DT_BF16 : GPT2_DT_F32;
+  const bool bf = c.compute != GPT2_FP32;  // 16-bit activations
+  const int adt = c.compute == GPT2_BF16 ? GPT2_DT_BF16 : c.compute == GPT2_FP16 ? GPT2_DT_F16 : GPT2_DT_F32;
   const size_t aes = bf ? 2 : 4;
   const int ldl = ((c.padded_vocab + 63) / 64) * 64;
 
@@ -243,7 +248,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t nflat = ((n + 63) / 64) * 64;
   size_t o_par = pl.raw(nflat * 4, "parameters"), o_grad = pl.raw(nflat * 4, "gradients");
   size_t o_m = pl.raw(nflat * 4, "adam_m"), o_v = pl.raw(nflat * 4, "adam_v");
-  size_t o_sh = bf ? pl.raw(nflat * 2, "bf16 weight copies") : 0;
+  size_t o_sh = bf ? pl.raw(nflat * 2, "16-bit weight copies") : 0;
   std::vector<size_t> toff(specs.size(), (size_t)-1);
   std::vector<int> tld(specs.size(), 0);
   size_t nt = 0;
@@ -254,7 +259,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     tld[j] = ld;
     nt += (size_t)specs[j].cols * ld;
   }
-  size_t o_sht = bf ? pl.raw(nt * 2 + 256, "transposed bf16 weight copies") : 0;
+  size_t o_sht = bf ? pl.raw(nt * 2 + 256, "transposed 16-bit weight copies") : 0;
   // tensor-table views of the flat arrays
   for (size_t j = 0; j < specs.size(); ++j) {
     auto& s = specs[j];
@@ -269,7 +274,7 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
       if (k == 4 && (!bf || !s.gemm_weight)) continue;
       t.name = std::string(pre[k]) + s.name;
       t.kind = k;
-      t.dtype = k == 4 ? GPT2_DT_BF16 : GPT2_DT_F32;
+      t.dtype = k == 4 ? adt : GPT2_DT_F32;
       size_t es = k == 4 ? 2 : 4;
       t.offset = base[k] + poff[j] * es;
       t.bytes = s.numel() * es;
@@ -326,7 +331,9 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     x->nflat = nflat;
     x->L = L; x->H = H; x->C = C; x->hd = C / H;
     x->V = c.vocab_size; x->Vp = c.padded_vocab; x->ldl = ldl; x->maxM = (int)maxM;
-    x->bf = bf; x->act_es = aes;
+    x->h16 = bf; x->act_es = aes;
+    x->dt = c.compute == GPT2_BF16 ? gk::ACT_BF16 : c.compute == GPT2_FP16 ? gk::ACT_F16 : gk::ACT_F32;
+    x->ls = c.compute == GPT2_FP16;
     x->params = (float*)(a + o_par); x->grads = (float*)(a + o_grad);
     x->am = (float*)(a + o_m); x->av = (float*)(a + o_v);
     x->shadow = bf ? (uint16_t*)(a + o_sh) : nullptr;
@@ -417,7 +424,7 @@ GemmArgs gemm_args(gpt2_ctx* c, int M, int N, int K, const void* A, int lda, boo
   a.kind = kind; a.out = out; a.ldo = ldo;
   a.out2 = nullptr; a.aux = nullptr; a.bias = nullptr;
   a.alpha = 1.f; a.beta = 0.f;
-  a.bf16 = c->bf;
+  a.dt = c->dt;
   a.splitk_ws = c->splitk_ws;
   a.splitk_ws_elems = c->splitk_elems;
   return a;
@@ -451,7 +458,7 @@ hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T, const DecodeAttn* 
   const float eps = c->cfg.ln_eps;
   {
     Timed t(c, GPT2_T_LN_FWD);
-    KCHK(gk::ln_fwd(c->h[2 * l], c->P(c->li(l, 0)), c->P(c->li(l, 1)), c->ln[2 * l], c->bf,
+    KCHK(gk::ln_fwd(c->h[2 * l], c->P(c->li(l, 0)), c->P(c->li(l, 1)), c->ln[2 * l], c->dt,
                     c->mean[2 * l], c->rstd[2 * l], M, C, eps, c->st));
   }
   GemmArgs g = gemm_args(c, M, 3 * C, C, c->ln[2 * l], C, false, c->W(c->li(l, 2)), C, false,
@@ -459,12 +466,12 @@ hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T, const DecodeAttn* 
   g.bias = c->P(c->li(l, 3));
   KCHK(run_gemm(c, g));
   if (dec) {
-    KCHK(gk::kv_store(c->qkv[l], dec->cache, B, 1, dec->t, c->cfg.max_seq, C, c->bf, c->st));
-    KCHK(gk::attn_decode(c->qkv[l], dec->cache, c->att[l], B, c->H, c->hd, c->cfg.max_seq, dec->t + 1, c->bf,
+    KCHK(gk::kv_store(c->qkv[l], dec->cache, B, 1, dec->t, c->cfg.max_seq, C, c->dt, c->st));
+    KCHK(gk::attn_decode(c->qkv[l], dec->cache, c->att[l], B, c->H, c->hd, c->cfg.max_seq, dec->t + 1, c->dt,
                          c->st));
   } else {
     Timed t(c, GPT2_T_ATTN_FWD);
-    KCHK(gk::attn_fwd(c->qkv[l], c->att[l], c->lse[l], B, T, c->H, c->hd, c->bf, c->st));
+    KCHK(gk::attn_fwd(c->qkv[l], c->att[l], c->lse[l], B, T, c->H, c->hd, c->dt, c->st));
   }
   g = gemm_args(c, M, C, C, c->att[l], C, false, c->W(c->li(l, 4)), C, false, gk::EPI_RESID,
                 c->h[2 * l + 1], C);
@@ -473,7 +480,7 @@ hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T, const DecodeAttn* 
   KCHK(run_gemm(c, g));
   {
     Timed t(c, GPT2_T_LN_FWD);
-    KCHK(gk::ln_fwd(c->h[2 * l + 1], c->P(c->li(l, 6)), c->P(c->li(l, 7)), c->ln[2 * l + 1], c->bf,
+    KCHK(gk::ln_fwd(c->h[2 * l + 1], c->P(c->li(l, 6)), c->P(c->li(l, 7)), c->ln[2 * l + 1], c->dt,
                     c->mean[2 * l + 1], c->rstd[2 * l + 1], M, C, eps, c->st));
   }
   g = gemm_args(c, M, 4 * C, C, c->ln[2 * l + 1], C, false, c->W(c->li(l, 8)), C, false,
@@ -491,7 +498,7 @@ hipError_t fwd_layer(gpt2_ctx* c, int l, int M, int B, int T, const DecodeAttn* 
 
 hipError_t ln_backward(gpt2_ctx* c, int k, int wj, const void* dy, bool accum, float beta, int M) {
   Timed t(c, GPT2_T_LN_BWD);
-  KCHK(gk::ln_bwd(c->h[k], c->mean[k], c->rstd[k], c->P(wj), dy, c->bf, c->dres, c->dres_act, accum,
+  KCHK(gk::ln_bwd(c->h[k], c->mean[k], c->rstd[k], c->P(wj), dy, c->dt, c->dres, c->dres_act, accum,
                   c->ln_part, M, c->C, c->st));
   return gk::ln_param_grad_reduce(c->ln_part, gk::ln_bwd_blocks(M), c->G(wj), c->G(wj + 1), c->C,
                                   beta, c->st);
@@ -499,14 +506,14 @@ hipError_t ln_backward(gpt2_ctx* c, int k, int wj, const void* dy, bool accum, f
 
 hipError_t colsum_timed(gpt2_ctx* c, const void* X, int M, int N, int ldx, float* db, float beta) {
   Timed t(c, GPT2_T_COLSUM);
-  return gk::colsum(X, c->bf, M, N, ldx, db, beta, c->col_part, c->st);
+  return gk::colsum(X, c->dt, M, N, ldx, db, beta, c->col_part, c->st);
 }
 
-// dX[M, in] = dY[M, out] W[out, in]: NT against the transposed copy in bf16,
+// dX[M, in] = dY[M, out] W[out, in]: NT against the transposed copy in 16 bits,
 // NN (B transposed in memory) in fp32.
 GemmArgs dx_args(gpt2_ctx* c, int M, int n_in, int n_out, const void* dY, int ldy, int wj, int kind,
                  void* out, int ldo) {
-  if (c->bf)
+  if (c->h16)
     return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->Wt(wj), c->tld[wj], false, kind, out, ldo);
   return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->W(wj), n_in, true, kind, out, ldo);
 }
@@ -544,7 +551,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   {
     Timed t(c, GPT2_T_ATTN_BWD);
     KCHK(gk::attn_bwd(c->qkv[l], c->att[l], c->dattn, c->lse[l], c->dqkv, c->attn_ws, B, T, c->H,
-                      c->hd, c->bf, c->st));
+                      c->hd, c->dt, c->st));
   }
   // qkv: da1 = dqkv W_qkv; dW_qkv = dqkv^T a1; db_qkv
   g = dx_args(c, M, C, 3 * C, c->dqkv, 3 * C, c->li(l, 2), gk::EPI_STORE, c->dA, C);
@@ -558,9 +565,9 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   return hipSuccess;
 }
 
-// Refreshes the transposed bf16 copies from the bf16 weight copies.
+// Refreshes the transposed 16-bit copies from the 16-bit weight copies.
 hipError_t refresh_transposed(gpt2_ctx* c) {
-  if (!c->bf) return hipSuccess;
+  if (!c->h16) return hipSuccess;
   Timed t(c, GPT2_T_TRANSPOSE);
   for (size_t j = 0; j < c->specs.size(); ++j) {
     if (c->toff[j] == (size_t)-1) continue;
@@ -585,7 +592,7 @@ hipError_t run_forward(gpt2_ctx* c, int B, int T, const int32_t* d_targets, bool
   const int lf = 2 + 12 * c->L;
   {
     Timed t(c, GPT2_T_LN_FWD);
-    KCHK(gk::ln_fwd(c->h[2 * c->L], c->P(lf), c->P(lf + 1), c->ln[2 * c->L], c->bf, c->mean[2 * c->L],
+    KCHK(gk::ln_fwd(c->h[2 * c->L], c->P(lf), c->P(lf + 1), c->ln[2 * c->L], c->dt, c->mean[2 * c->L],
                     c->rstd[2 * c->L], M, C, c->cfg.ln_eps, c->st));
   }
   GemmArgs g = gemm_args(c, M, c->Vp, C, c->ln[2 * c->L], C, false, c->W(0), C, false, gk::EPI_LOGITS,
@@ -594,8 +601,8 @@ hipError_t run_forward(gpt2_ctx* c, int B, int T, const int32_t* d_targets, bool
   if (d_targets) {
     {
       Timed t(c, GPT2_T_XENT);
-      KCHK(gk::xent(c->logits, c->bf, c->ldl, c->Vp, c->V, d_targets, c->losses, 1.0f / (float)M, want_grad,
-                    M, c->flag, c->st));
+      KCHK(gk::xent(c->logits, c->dt, c->ldl, c->Vp, c->V, d_targets, c->losses, 1.0f / (float)M, want_grad,
+                    M, c->flag, c->ls ? c->scal + 10 : nullptr, c->st));
     }
     KCHK(gk::loss_reduce(c->losses, M, c->scal + 8, c->flag, c->st));
   }
@@ -731,8 +738,14 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
     return bail(e, "zero logits");
   for (const Guard& g : c->guards)
     if ((e = hipMemsetAsync(c->arena + g.offset, kGuardByte, kGuard, c->st))) return bail(e, "guards");
-  if (c->bf && (e = gk::to_bf16(c->params, c->shadow, c->nflat, c->st))) return bail(e, "bf16 copy");
-  if (c->bf && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
+  if (c->h16 && (e = gk::to_h16(c->params, c->shadow, c->nflat, c->dt, c->st))) return bail(e, "16-bit copy");
+  if (c->h16 && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
+  if (c->ls) {  // dynamic loss scale and its step counter
+    c->ls_staging[0] = 65536.f;
+    c->ls_staging[1] = 0.f;
+    if ((e = hipMemcpyAsync(c->scal + 10, c->ls_staging, 8, hipMemcpyHostToDevice, c->st)))
+      return bail(e, "loss scale");
+  }
   if ((e = refresh_transposed(c))) return bail(e, "transposed copies");
   // AdamW chunk table
   std::vector<gk::AdamChunk> ch;
@@ -744,7 +757,7 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
       gk::AdamChunk a;
       a.start = c->poff[j] + i;
       a.count = (uint32_t)std::min(CH, n - i);
-      a.flags = (s.decay ? 1u : 0u) | ((c->bf && s.gemm_weight) ? 2u : 0u);
+      a.flags = (s.decay ? 1u : 0u) | ((c->h16 && s.gemm_weight) ? 2u : 0u);
       ch.push_back(a);
     }
   }
@@ -826,7 +839,7 @@ GPT2_API gpt2_status gpt2_eval_loss(gpt2_ctx* c, const int32_t* d_tokens, const 
 
 GPT2_API size_t gpt2_kv_cache_bytes(const gpt2_config* cfg) {
   if (!config_ok(cfg, nullptr)) return 0;
-  const size_t es = cfg->compute == GPT2_BF16 ? 2 : 4;
+  const size_t es = cfg->compute == GPT2_FP32 ? 4 : 2;
   return (size_t)cfg->n_layer * cfg->max_batch * cfg->max_seq * 2 * cfg->n_embd * es;
 }
 
@@ -849,8 +862,8 @@ GPT2_API gpt2_status gpt2_generate(gpt2_ctx* c, void* d_kv_cache, size_t kv_byte
   HIPCHK(c, hipMemcpy2DAsync(c->tok, (size_t)T0 * 4, d_tokens, (size_t)T_total * 4, (size_t)T0 * 4, B,
                              hipMemcpyDeviceToDevice, c->st));
   HIPCHK(c, run_forward(c, B, T0, nullptr, false));
-  for (int l = 0; l < L; ++l) HIPCHK(c, gk::kv_store(c->qkv[l], cache(l), B, T0, 0, c->cfg.max_seq, C, c->bf, c->st));
-  HIPCHK(c, gk::sample(c->logits, c->bf, c->ldl, T0, T0 - 1, c->V, B, d_uniform, n_new, d_tokens + T0, T_total,
+  for (int l = 0; l < L; ++l) HIPCHK(c, gk::kv_store(c->qkv[l], cache(l), B, T0, 0, c->cfg.max_seq, C, c->dt, c->st));
+  HIPCHK(c, gk::sample(c->logits, c->dt, c->ldl, T0, T0 - 1, c->V, B, d_uniform, n_new, d_tokens + T0, T_total,
                        d_logprob, n_new, c->st));
   // decode: one position per sequence per step, attention over the cache
   const int lf = 2 + 12 * L;
@@ -862,13 +875,13 @@ GPT2_API gpt2_status gpt2_generate(gpt2_ctx* c, void* d_kv_cache, size_t kv_byte
       DecodeAttn d{cache(l), t};
       HIPCHK(c, fwd_layer(c, l, B, B, 1, &d));
     }
-    HIPCHK(c, gk::ln_fwd(c->h[2 * L], c->P(lf), c->P(lf + 1), c->ln[2 * L], c->bf, c->mean[2 * L],
+    HIPCHK(c, gk::ln_fwd(c->h[2 * L], c->P(lf), c->P(lf + 1), c->ln[2 * L], c->dt, c->mean[2 * L],
                          c->rstd[2 * L], B, C, c->cfg.ln_eps, c->st));
     GemmArgs g = gemm_args(c, B, c->Vp, C, c->ln[2 * L], C, false, c->W(0), C, false, gk::EPI_LOGITS, c->logits,
                            c->ldl);
     HIPCHK(c, run_gemm(c, g));
     const int k = t + 1 - T0;
-    HIPCHK(c, gk::sample(c->logits, c->bf, c->ldl, 1, 0, c->V, B, d_uniform + k, n_new, d_tokens + t + 1,
+    HIPCHK(c, gk::sample(c->logits, c->dt, c->ldl, 1, 0, c->V, B, d_uniform + k, n_new, d_tokens + t + 1,
                          T_total, d_logprob ? d_logprob + k : nullptr, n_new, c->st));
   }
   int flags = 0;
@@ -924,11 +937,11 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
     Timed t(c, GPT2_T_NORM);
     HIPCHK(c, gk::sumsq(c->grads, c->nflat, c->norm_part, c->st));
     HIPCHK(c, gk::norm_finalize(c->norm_part, gk::sumsq_blocks(), clip, c->cfg.beta1, c->cfg.beta2,
-                                c->scal, c->flag, c->st));
+                                c->scal, c->flag, c->ls, c->ls_interval, c->st));
   }
   {
     Timed t(c, GPT2_T_ADAMW);
-    HIPCHK(c, gk::adamw(c->params, c->grads, c->am, c->av, c->shadow, c->chunks, c->nchunks, c->scal,
+    HIPCHK(c, gk::adamw(c->params, c->grads, c->am, c->av, c->shadow, c->dt, c->chunks, c->nchunks, c->scal,
                         lr, c->cfg.beta1, c->cfg.beta2, c->cfg.adam_eps, c->cfg.weight_decay, c->st));
   }
   HIPCHK(c, refresh_transposed(c));
@@ -940,7 +953,35 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
     s = read_flags(c, &flags);
     if (s) return s;
     if (flags & 8) return fail(c, GPT2_E_NONFINITE, "non-finite gradient norm; update skipped");
+    if (flags & 16) *h_grad_norm = INFINITY;  // fp16 overflow: skipped, loss scale halved
   }
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_get_loss_scale(gpt2_ctx* c, float* scale) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (!scale) return fail(c, GPT2_E_ARG, "NULL output");
+  if (!c->ls) {
+    *scale = 1.f;
+    return GPT2_OK;
+  }
+  HIPCHK(c, hipMemcpyAsync(scale, c->scal + 10, 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return GPT2_OK;
+}
+
+GPT2_API gpt2_status gpt2_set_loss_scale(gpt2_ctx* c, float scale, int32_t growth_interval) {
+  gpt2_status s = check_ctx(c);
+  if (s) return s;
+  if (!c->ls) return fail(c, GPT2_E_ARG, "loss scaling is the fp16 compute mode's");
+  if (!(scale > 0.f) || !std::isfinite(scale) || growth_interval < 1)
+    return fail(c, GPT2_E_ARG, "scale must be finite and > 0, growth_interval >= 1");
+  c->ls_interval = growth_interval;
+  c->ls_staging[0] = scale;
+  c->ls_staging[1] = 0.f;
+  HIPCHK(c, hipMemcpyAsync(c->scal + 10, c->ls_staging, 8, hipMemcpyHostToDevice, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
   return GPT2_OK;
 }
 
@@ -969,7 +1010,7 @@ GPT2_API gpt2_status gpt2_block_fwd_bwd(gpt2_ctx* c, int32_t layer, const float*
   HIPCHK(c, fwd_layer(c, layer, M, B, T));
   HIPCHK(c, hipMemcpyAsync(d_y, c->h[2 * layer + 2], bytes, hipMemcpyDeviceToDevice, c->st));
   HIPCHK(c, hipMemcpyAsync(c->dres, d_dy, bytes, hipMemcpyDeviceToDevice, c->st));
-  HIPCHK(c, gk::copy_f32_to_act(c->dres, c->dres_act, c->bf, (size_t)M * c->C, c->st));
+  HIPCHK(c, gk::copy_f32_to_act(c->dres, c->dres_act, c->dt, (size_t)M * c->C, c->st));
   HIPCHK(c, bwd_layer(c, layer, M, B, T, 0.f));
   HIPCHK(c, hipMemcpyAsync(d_dx, c->dres, bytes, hipMemcpyDeviceToDevice, c->st));
   return GPT2_OK;
@@ -1001,7 +1042,7 @@ GPT2_API gpt2_status gpt2_check_arena(gpt2_ctx* c, int32_t* n_bad) {
 GPT2_API gpt2_status gpt2_sync_weight_copies(gpt2_ctx* c) {
   gpt2_status s = check_ctx(c);
   if (s) return s;
-  if (c->bf) HIPCHK(c, gk::to_bf16(c->params, c->shadow, c->nflat, c->st));
+  if (c->h16) HIPCHK(c, gk::to_h16(c->params, c->shadow, c->nflat, c->dt, c->st));
   HIPCHK(c, refresh_transposed(c));
   return GPT2_OK;
 }

@@ -2,8 +2,9 @@
 //   forward  Y = X W^T   (A, B both K-contiguous)
 //   dX       dX = dY W   (B operand transposed in memory)
 //   dW       dW = dY^T X (both operands transposed in memory)
-// bf16 operands run on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation).  Tiles are staged global -> registers -> LDS with a
+// 16-bit operands (bf16, or fp16 for the fp16 workload) run on the gfx950
+// matrix cores (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation).
+// Tiles are staged global -> registers -> LDS with a
 // double-buffered LDS ring; operands that are contiguous along M/N instead
 // of K are loaded as 8x8 blocks and transposed in registers (v_perm), so the
 // LDS always holds [row][k] and every MFMA fragment is one 16-byte LDS read.
@@ -65,8 +66,8 @@ __device__ __forceinline__ void epi_store(const GP& p, int r, int c, float acc) 
   }
 }
 
-// Four consecutive output columns c..c+3 of row r (bf16 activations).
-template <int EPI>
+// Four consecutive output columns c..c+3 of row r (16-bit activations TE).
+template <int EPI, typename TE>
 __device__ __forceinline__ void epi_store4(const GP& p, int r, int c, float v0, float v1, float v2,
                                            float v3) {
   if (r >= p.M) return;
@@ -74,34 +75,34 @@ __device__ __forceinline__ void epi_store4(const GP& p, int r, int c, float v0, 
     const float v[4] = {v0, v1, v2, v3};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (c + j < p.N) epi_store<EPI, bf16>(p, r, c + j, v[j]);
+      if (c + j < p.N) epi_store<EPI, TE>(p, r, c + j, v[j]);
     return;
   }
   const size_t o = (size_t)r * p.ldo + c;
   if constexpr (EPI == EPI_STORE) {
     float4 b = p.bias ? *(const float4*)(p.bias + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(p.alpha * v0 + b.x, p.alpha * v1 + b.y),
-                                             pack_bf2(p.alpha * v2 + b.z, p.alpha * v3 + b.w));
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(p.alpha * v0 + b.x, p.alpha * v1 + b.y),
+                                             H16<TE>::pack2(p.alpha * v2 + b.z, p.alpha * v3 + b.w));
   } else if constexpr (EPI == EPI_LOGITS) {
-    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(v0, v1), H16<TE>::pack2(v2, v3));
   } else if constexpr (EPI == EPI_GELU) {
     float4 b = *(const float4*)(p.bias + c);
     float u0 = v0 + b.x, u1 = v1 + b.y, u2 = v2 + b.z, u3 = v3 + b.w;
-    *(uint2*)((bf16*)p.out + o) = make_uint2(pack_bf2(u0, u1), pack_bf2(u2, u3));
-    *(uint2*)((bf16*)p.out2 + o) = make_uint2(pack_bf2(gelu_tanh_f(u0), gelu_tanh_f(u1)),
-                                              pack_bf2(gelu_tanh_f(u2), gelu_tanh_f(u3)));
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(u0, u1), H16<TE>::pack2(u2, u3));
+    *(uint2*)((TE*)p.out2 + o) = make_uint2(H16<TE>::pack2(gelu_tanh_f(u0), gelu_tanh_f(u1)),
+                                              H16<TE>::pack2(gelu_tanh_f(u2), gelu_tanh_f(u3)));
   } else if constexpr (EPI == EPI_RESID) {
     float4 b = *(const float4*)(p.bias + c);
     float4 x = *(const float4*)((const float*)p.aux + o);
     *(float4*)((float*)p.out + o) = make_float4(x.x + v0 + b.x, x.y + v1 + b.y, x.z + v2 + b.z,
                                                 x.w + v3 + b.w);
   } else if constexpr (EPI == EPI_DGELU) {
-    uint2 uu = *(const uint2*)((const bf16*)p.aux + o);
-    float u0 = bfbits2f(uu.x & 0xffffu), u1 = bfbits2f(uu.x >> 16);
-    float u2 = bfbits2f(uu.y & 0xffffu), u3 = bfbits2f(uu.y >> 16);
-    *(uint2*)((bf16*)p.out + o) =
-        make_uint2(pack_bf2(v0 * gelu_tanh_grad_f(u0), v1 * gelu_tanh_grad_f(u1)),
-                   pack_bf2(v2 * gelu_tanh_grad_f(u2), v3 * gelu_tanh_grad_f(u3)));
+    uint2 uu = *(const uint2*)((const TE*)p.aux + o);
+    float u0 = H16<TE>::lo(uu.x), u1 = H16<TE>::hi(uu.x);
+    float u2 = H16<TE>::lo(uu.y), u3 = H16<TE>::hi(uu.y);
+    *(uint2*)((TE*)p.out + o) =
+        make_uint2(H16<TE>::pack2(v0 * gelu_tanh_grad_f(u0), v1 * gelu_tanh_grad_f(u1)),
+                   H16<TE>::pack2(v2 * gelu_tanh_grad_f(u2), v3 * gelu_tanh_grad_f(u3)));
   } else {  // EPI_WGRAD
     float* op = (float*)p.out + (size_t)blockIdx.z * ((size_t)p.M * p.ldo);
     if (gridDim.z > 1) {
@@ -117,13 +118,13 @@ __device__ __forceinline__ void epi_store4(const GP& p, int r, int c, float v0, 
   }
 }
 
-// ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BK = 64;       // K tile (bf16 elements)
+// ------------------------------------------------------------------ 16-bit MFMA kernel
+constexpr int BK = 64;       // K tile (16-bit elements)
 constexpr int LDS_LD = 72;   // padded LDS row (elements): 144 B, 16-byte aligned
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*)p; }
 
-// Transpose of a KR x 8 block of bf16 (KR = 4 or 8): in[i] holds the 8
+// Transpose of a KR x 8 block of 16-bit values (KR = 4 or 8): in[i] holds the 8
 // row values of k = i; out[r] (KR/2 dwords) holds the KR k values of row r.
 template <int KR>
 __device__ __forceinline__ void transpose_block(const uint4 (&in)[KR], uint32_t (&out)[8][KR / 2]) {
@@ -242,8 +243,9 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int& tm, int& tn) {
   tn = in / gsz;
 }
 
-template <int BM, int BN, int WM, int WN, bool AT, bool BT, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
+template <typename TE, int BM, int BN, int WM, int WN, bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void k_gemm_h16(GP p) {
+  typedef typename H16<TE>::v8 v8;
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 fragments per wave
@@ -284,18 +286,18 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
   // D = B_frag x A_frag: the accumulator is the transposed 32x32 block, so a
   // lane holds one output row and 4 runs of 4 consecutive output columns.
   auto substep = [&](const uint16_t* As, const uint16_t* Bs, int ks) {
-    bf16x8 af[FM], bfr[FN];
+    v8 af[FM], bfr[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      af[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (wm + i * 32 + fr) * LDS_LD + ks * 16 + fk));
+      af[i] = __builtin_bit_cast(v8, *(const uint4*)(As + (wm + i * 32 + fr) * LDS_LD + ks * 16 + fk));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      bfr[j] = __builtin_bit_cast(bf16x8, *(const uint4*)(Bs + (wn + j * 32 + fr) * LDS_LD + ks * 16 + fk));
+      bfr[j] = __builtin_bit_cast(v8, *(const uint4*)(Bs + (wn + j * 32 + fr) * LDS_LD + ks * 16 + fk));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = H16<TE>::mfma(bfr[j], af[i], acc[i][j]);
   };
 
   for (int kt = 0; kt < nk; ++kt) {
@@ -325,12 +327,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_bf16(GP p) {
       for (int e4 = 0; e4 < 4; ++e4) {
         int r = m0 + wm + i * 32 + fr;
         int c = n0 + wn + j * 32 + e4 * 8 + (lane >> 5) * 4;
-        epi_store4<EPI>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
-                        acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+        epi_store4<EPI, TE>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                            acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
       }
 }
 
-// ------------------------------------------------------------------ bf16 NT kernel, direct-to-LDS
+// ------------------------------------------------------------------ 16-bit NT kernel, direct-to-LDS
 // Both operands K-contiguous.  Persistent workgroups walk an XCD-grouped
 // tile order; the K loop runs in stages of 32 k held in an NS-deep LDS ring
 // that global_load_lds_dwordx4 fills directly (no VGPR staging), NS - 1
@@ -439,12 +441,13 @@ __device__ __forceinline__ void grouped_coords(int pid, int nm, int nn, int& tm,
   tn = in / gsz;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <typename TE, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
+  typedef typename H16<TE>::v8 v8;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int STAGE = (BM + BN) * NK;  // bf16 elements per stage
+  constexpr int STAGE = (BM + BN) * NK;  // 16-bit elements per stage
   constexpr int PER = BufLoader<BM, NW>::NI + BufLoader<BN, NW>::NI;  // loads per stage
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
 
@@ -503,24 +506,24 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  bf16x8 af[2][FM], bfr[2][FN];
+  v8 af[2][FM], bfr[2][FN];
   auto load_frags = [&](int t, int ks, int set) {
     const uint16_t* As = lds + (t % NS) * STAGE;
     const uint16_t* Bs = As + BM * NK;
     const int slot = (ks * 2 + g) ^ swz;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      af[set][i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + ((wm + i * 32 + fr) * 4 + slot) * 8));
+      af[set][i] = __builtin_bit_cast(v8, *(const uint4*)(As + ((wm + i * 32 + fr) * 4 + slot) * 8));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      bfr[set][j] = __builtin_bit_cast(bf16x8, *(const uint4*)(Bs + ((wn + j * 32 + fr) * 4 + slot) * 8));
+      bfr[set][j] = __builtin_bit_cast(v8, *(const uint4*)(Bs + ((wn + j * 32 + fr) * 4 + slot) * 8));
   };
   auto mfma_set = [&](int set) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = H16<TE>::mfma(bfr[set][j], af[set][i], acc[i][j]);
   };
 
   // Stage s + 1 is made visible (wait + barrier) one stage early, so the
@@ -555,8 +558,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
         for (int e4 = 0; e4 < 4; ++e4) {
           int r = m0 + wm + i * 32 + fr;
           int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
-          epi_store4<EPI>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
-                          acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+          epi_store4<EPI, TE>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                              acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   }
 }
 
-// ------------------------------------------------------------------ bf16 TN kernel (weight gradients)
+// ------------------------------------------------------------------ 16-bit TN kernel (weight gradients)
 // D[r][c] = sum_m A[m * lda + r] * B[m * ldb + c]: both operands keep their
 // natural [token][feature] layout.  Stages of 32 tokens are loaded straight
 // into LDS (buffer loads whose descriptor starts at the stage's first token,
@@ -611,7 +614,7 @@ struct TokLoader {
 // 8 k values (tokens ks*16 + 8g .. +7) of feature column `col` of an LDS tile
 // [32][COLS], as an MFMA operand; lane l serves column base + l % 32.
 template <int COLS>
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int cbase, int ks, int lane) {
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int cbase, int ks, int lane) {
   const int G = lane >> 4, q = lane & 15;
   const int col = cbase + 16 * (G & 1) + 4 * (q & 3);
   v4s h[2];
@@ -621,14 +624,15 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int cbase, int k
     const int off = m * COLS + (((col >> 3) ^ (4 * (m & 3))) << 3) + (col & 7);
     h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
   }
-  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
-                                                 __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
-                                                 __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
-                                                 __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]})));
+  return make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]}));
 }
 
-template <int BM, int BN, int WM, int WN>
+template <typename TE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
+  typedef typename H16<TE>::v8 v8;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -701,21 +705,21 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  bf16x8 af[2][FM], bfr[2][FN];
+  v8 af[2][FM], bfr[2][FN];
   auto load_frags = [&](int t, int ks, int set) {
     const uint16_t* As = lds + (t % NS) * STAGE;
     const uint16_t* Bs = As + BM * TK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[set][i] = tr_frag<BM>(As, wm + i * 32, ks, lane);
+    for (int i = 0; i < FM; ++i) af[set][i] = __builtin_bit_cast(v8, tr_frag<BM>(As, wm + i * 32, ks, lane));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[set][j] = tr_frag<BN>(Bs, wn + j * 32, ks, lane);
+    for (int j = 0; j < FN; ++j) bfr[set][j] = __builtin_bit_cast(v8, tr_frag<BN>(Bs, wn + j * 32, ks, lane));
   };
   auto mfma_set = [&](int set) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = H16<TE>::mfma(bfr[set][j], af[set][i], acc[i][j]);
   };
 
   if (total > 0) {
@@ -1040,18 +1044,18 @@ size_t gemm_splitk_ws_elems(int M, int N, int K) {
   return a > b ? a : b;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <typename TE, int BM, int BN, int WM, int WN>
 static void launch_tn(GP q, int per_cu, hipStream_t st) {
   long items = (long)cdiv(q.M, BM) * cdiv(q.N, BN) * q.splits;
   long cap = 256L * per_cu;
   int grid = (int)(items < cap ? ((items + 7) / 8) * 8 : cap);
-  k_gemm_tn<BM, BN, WM, WN><<<grid, WM * WN * 64, 0, st>>>(q);
+  k_gemm_tn<TE, BM, BN, WM, WN><<<grid, WM * WN * 64, 0, st>>>(q);
 }
 
-template <int BM, int BN, bool AT, bool BT, int EPI>
+template <typename TE, int BM, int BN, bool AT, bool BT, int EPI>
 static void launch_cfg(GP q, int S, hipStream_t st) {
   int nb = cdiv(q.M, BM) * cdiv(q.N, BN);
-  k_gemm_bf16<BM, BN, 2, 2, AT, BT, EPI><<<dim3(nb, 1, S), 256, 0, st>>>(q);
+  k_gemm_h16<TE, BM, BN, 2, 2, AT, BT, EPI><<<dim3(nb, 1, S), 256, 0, st>>>(q);
 }
 
 // NT tile choice: 256x256 (8 waves), 256x192 or 256x128 (4 waves), by the
@@ -1073,15 +1077,15 @@ static int plan_nt(int M, int N) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <typename TE, int BM, int BN, int WM, int WN, int EPI>
 static void launch_nt(GP q, hipStream_t st) {
   int tiles = cdiv(q.M, BM) * cdiv(q.N, BN);
   int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
-  k_gemm_nt<BM, BN, WM, WN, EPI><<<grid, WM * WN * 64, 0, st>>>(q);
+  k_gemm_nt<TE, BM, BN, WM, WN, EPI><<<grid, WM * WN * 64, 0, st>>>(q);
 }
 
-template <bool AT, bool BT, int EPI>
-static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
+template <typename TE, bool AT, bool BT, int EPI>
+static hipError_t launch_h16(const GemmArgs& a, GP p, hipStream_t st) {
   if constexpr (AT && BT && EPI == EPI_WGRAD) {
     if (a.N % 4 == 0 && a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws) {
       TnPlan tp = plan_tn(a.M, a.N, a.K, a.splitk_ws_elems);
@@ -1090,9 +1094,9 @@ static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
       GP q = p;
       if (tp.splits > 1) q.out = a.splitk_ws;
       switch (tp.cfg) {
-        case 0: launch_tn<256, 256, 4, 2>(q, 1, st); break;
-        case 1: launch_tn<256, 128, 2, 2>(q, 1, st); break;
-        default: launch_tn<128, 128, 2, 2>(q, 2, st); break;
+        case 0: launch_tn<TE, 256, 256, 4, 2>(q, 1, st); break;
+        case 1: launch_tn<TE, 256, 128, 2, 2>(q, 1, st); break;
+        default: launch_tn<TE, 128, 128, 2, 2>(q, 2, st); break;
       }
       if (tp.splits > 1) {
         size_t n = (size_t)a.M * a.N;
@@ -1105,9 +1109,9 @@ static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
     if (a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
       p.kchunk = a.K;
       switch (plan_nt(a.M, a.N)) {
-        case 0: launch_nt<256, 256, 4, 2, EPI>(p, st); break;
-        case 1: launch_nt<256, 192, 2, 2, EPI>(p, st); break;
-        default: launch_nt<256, 128, 2, 2, EPI>(p, st); break;
+        case 0: launch_nt<TE, 256, 256, 4, 2, EPI>(p, st); break;
+        case 1: launch_nt<TE, 256, 192, 2, 2, EPI>(p, st); break;
+        default: launch_nt<TE, 256, 128, 2, 2, EPI>(p, st); break;
       }
       return hipGetLastError();
     }
@@ -1118,10 +1122,10 @@ static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
   GP q = p;
   if (pl.splits > 1) q.out = a.splitk_ws;
   switch (pl.cfg) {
-    case 0: launch_cfg<256, 256, AT, BT, EPI>(q, pl.splits, st); break;
-    case 1: launch_cfg<256, 192, AT, BT, EPI>(q, pl.splits, st); break;
-    case 2: launch_cfg<256, 128, AT, BT, EPI>(q, pl.splits, st); break;
-    default: launch_cfg<128, 128, AT, BT, EPI>(q, pl.splits, st); break;
+    case 0: launch_cfg<TE, 256, 256, AT, BT, EPI>(q, pl.splits, st); break;
+    case 1: launch_cfg<TE, 256, 192, AT, BT, EPI>(q, pl.splits, st); break;
+    case 2: launch_cfg<TE, 256, 128, AT, BT, EPI>(q, pl.splits, st); break;
+    default: launch_cfg<TE, 128, 128, AT, BT, EPI>(q, pl.splits, st); break;
   }
   if (pl.splits > 1) {
     size_t n = (size_t)a.M * a.N;
@@ -1133,7 +1137,7 @@ static hipError_t launch_bf16(const GemmArgs& a, GP p, hipStream_t st) {
 // fp32 problems of 2^27 multiply-adds or more go to the matrix cores; the
 // small ones (the tiny model) keep the FMA kernel.  Weight gradients split K
 // (the tokens) so that the grid covers the 256 CUs, summed by the same
-// fixed-order reduction as the bf16 path.
+// fixed-order reduction as the 16-bit path.
 template <bool AT, bool BT, int EPI>
 static hipError_t launch_f32(const GemmArgs& a, GP p, hipStream_t st) {
   if ((double)a.M * a.N * a.K >= 134217728.0) {
@@ -1166,13 +1170,22 @@ static hipError_t dispatch_t(const GemmArgs& a, const GP& p, hipStream_t st) {
                         EPI == EPI_DGELU;
   constexpr bool NN_OK = EPI == EPI_STORE || EPI == EPI_DGELU;
   constexpr bool TN_OK = EPI == EPI_WGRAD;
-  if (a.bf16) {
+  if (a.dt == ACT_BF16) {
     if constexpr (NT_OK)
-      if (!a.a_t && !a.b_t) return launch_bf16<false, false, EPI>(a, p, st);
+      if (!a.a_t && !a.b_t) return launch_h16<bf16, false, false, EPI>(a, p, st);
     if constexpr (NN_OK)
-      if (!a.a_t && a.b_t) return launch_bf16<false, true, EPI>(a, p, st);
+      if (!a.a_t && a.b_t) return launch_h16<bf16, false, true, EPI>(a, p, st);
     if constexpr (TN_OK)
-      if (a.a_t && a.b_t) return launch_bf16<true, true, EPI>(a, p, st);
+      if (a.a_t && a.b_t) return launch_h16<bf16, true, true, EPI>(a, p, st);
+    return hipErrorInvalidValue;
+  }
+  if (a.dt == ACT_F16) {
+    if constexpr (NT_OK)
+      if (!a.a_t && !a.b_t) return launch_h16<f16, false, false, EPI>(a, p, st);
+    if constexpr (NN_OK)
+      if (!a.a_t && a.b_t) return launch_h16<f16, false, true, EPI>(a, p, st);
+    if constexpr (TN_OK)
+      if (a.a_t && a.b_t) return launch_h16<f16, true, true, EPI>(a, p, st);
     return hipErrorInvalidValue;
   }
   if constexpr (NT_OK)

@@ -19,7 +19,7 @@ GPT2_OK, GPT2_E_ARG, GPT2_E_SHAPE, GPT2_E_STATE = 0, -1, -2, -3
 GPT2_E_HIP, GPT2_E_TOKEN, GPT2_E_NONFINITE, GPT2_E_ARENA = -4, -5, -6, -7
 STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_STATE", -4: "E_HIP", -5: "E_TOKEN",
           -6: "E_NONFINITE", -7: "E_ARENA"}
-GPT2_FP32, GPT2_BF16 = 0, 1
+GPT2_FP32, GPT2_BF16, GPT2_FP16 = 0, 1, 2
 KINDS = ["param", "grad", "adam_m", "adam_v", "shadow", "act", "logits", "scalar"]
 TIMING = {"none": 0, "lmhead_fwd": 1, "gemm": 2, "attn_fwd": 3, "attn_bwd": 4, "ln_fwd": 5,
           "ln_bwd": 6, "xent": 7, "adamw": 8, "norm": 9, "transpose": 10, "embed": 11,
@@ -31,7 +31,7 @@ EXPORTS = ["gpt2_default_config", "gpt2_arena_bytes", "gpt2_num_params", "gpt2_i
            "gpt2_zero_grad", "gpt2_step", "gpt2_lr_at", "gpt2_block_fwd_bwd", "gpt2_num_tensors",
            "gpt2_tensor_info", "gpt2_timing_enable", "gpt2_timing_read", "gpt2_sync_weight_copies",
            "gpt2_get_step_count", "gpt2_set_step_count", "gpt2_check_arena", "gpt2_eval_loss",
-           "gpt2_kv_cache_bytes", "gpt2_generate"]
+           "gpt2_kv_cache_bytes", "gpt2_generate", "gpt2_get_loss_scale", "gpt2_set_loss_scale"]
 
 
 class Config(ct.Structure):
@@ -87,6 +87,8 @@ def bind(L):
         "gpt2_eval_loss": (I32, [P, P, P, I32, I32, ct.POINTER(F)]),
         "gpt2_kv_cache_bytes": (SZ, [cfgp]),
         "gpt2_generate": (I32, [P, P, SZ, P, I32, I32, I32, P, P]),
+        "gpt2_get_loss_scale": (I32, [P, ct.POINTER(F)]),
+        "gpt2_set_loss_scale": (I32, [P, F, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -112,7 +114,7 @@ def make_config(n_layer, n_head, n_embd, block_size, vocab_size, padded_vocab, m
     lib().gpt2_default_config(ct.byref(c), max_batch, max_seq)
     c.n_layer, c.n_head, c.n_embd = n_layer, n_head, n_embd
     c.block_size, c.vocab_size, c.padded_vocab = block_size, vocab_size, padded_vocab
-    c.compute = GPT2_BF16 if compute == "bf16" else GPT2_FP32
+    c.compute = {"bf16": GPT2_BF16, "fp16": GPT2_FP16, "fp32": GPT2_FP32}[compute]
     return c
 
 
@@ -249,6 +251,14 @@ class GPT2Step:
         n = ct.c_int32(0)
         self._check(self._L.gpt2_check_arena(self.ctx, ct.byref(n)))
 
+    def loss_scale(self):
+        v = ct.c_float(0.0)
+        self._check(self._L.gpt2_get_loss_scale(self.ctx, ct.byref(v)))
+        return v.value
+
+    def set_loss_scale(self, scale: float, growth_interval: int = 2000):
+        self._check(self._L.gpt2_set_loss_scale(self.ctx, scale, growth_interval))
+
     def sync_weight_copies(self):
         self._check(self._L.gpt2_sync_weight_copies(self.ctx))
 
@@ -282,7 +292,8 @@ class GPT2Step:
         """Zero-copy torch view of a tensor in the arena."""
         t = self.tensors[name]
         torch = self.torch
-        dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32, 3: torch.float64}[t["dtype"]]
+        dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32, 3: torch.float64,
+              4: torch.float16}[t["dtype"]]
         raw = self.arena[t["offset"]:t["offset"] + t["bytes"]]
         return raw.view(dt).view(t["shape"])
 

@@ -61,9 +61,14 @@ typedef enum {
 } gpt2_status;
 
 typedef enum {
-  GPT2_FP32 = 0,  /* fp32 storage and arithmetic throughout */
-  GPT2_BF16 = 1   /* bf16 GEMM/attention operands, fp32 accumulation,
+  GPT2_FP32 = 0,  /* fp32 storage and arithmetic throughout (GEMMs of 2^27
+                     multiply-adds or more on the fp32 matrix cores) */
+  GPT2_BF16 = 1,  /* bf16 GEMM/attention operands, fp32 accumulation,
                      fp32 residual stream, master weights and optimizer */
+  GPT2_FP16 = 2   /* as GPT2_BF16 with fp16 (IEEE half) operands, plus dynamic
+                     loss scaling ("Let's reproduce GPT-2 (124M)" chapter
+                     "float16, gradient scalers, bfloat16"): see
+                     gpt2_get_loss_scale */
 } gpt2_compute;
 
 typedef struct {
@@ -89,7 +94,7 @@ typedef struct gpt2_ctx gpt2_ctx;
 /* Tensor kinds and dtypes reported by gpt2_tensor_info. */
 enum { GPT2_K_PARAM = 0, GPT2_K_GRAD = 1, GPT2_K_ADAM_M = 2, GPT2_K_ADAM_V = 3,
        GPT2_K_SHADOW = 4, GPT2_K_ACT = 5, GPT2_K_LOGITS = 6, GPT2_K_SCALAR = 7 };
-enum { GPT2_DT_F32 = 0, GPT2_DT_BF16 = 1, GPT2_DT_I32 = 2, GPT2_DT_F64 = 3 };
+enum { GPT2_DT_F32 = 0, GPT2_DT_BF16 = 1, GPT2_DT_I32 = 2, GPT2_DT_F64 = 3, GPT2_DT_F16 = 4 };
 
 typedef struct {
   char name[48];
@@ -193,6 +198,20 @@ gpt2_status gpt2_zero_grad(gpt2_ctx* c);
  * given, synchronizes once and returns the pre-clip norm; a non-finite norm
  * is then reported as GPT2_E_NONFINITE. */
 gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_norm);
+
+/* Dynamic loss scaling (GPT2_FP16 only).  The logits gradient is multiplied
+ * by the loss scale S (device-resident, 65536 after gpt2_create), so the
+ * fp16 gradients of backward carry S; gpt2_step divides it out of the norm
+ * (the reported norm is the unscaled one) and out of the AdamW update.  If
+ * the scaled gradients overflow (non-finite norm), the step is skipped on
+ * the device (parameters, moments and step count unchanged), S is halved,
+ * and gpt2_step returns GPT2_OK with *h_grad_norm = +inf.  After
+ * growth_interval (2000 after create) consecutive finite steps S doubles.
+ * get: synchronizes and reads S (1 for the other compute modes).
+ * set: sets S and growth_interval and restarts the interval count; fp16
+ * only (GPT2_E_ARG otherwise); S finite and > 0, growth_interval >= 1. */
+gpt2_status gpt2_get_loss_scale(gpt2_ctx* c, float* scale);
+gpt2_status gpt2_set_loss_scale(gpt2_ctx* c, float scale, int32_t growth_interval);
 
 /* Learning rate at optimizer iteration it (0-based), "Let's reproduce GPT-2
  * (124M)" key takeaways, bullet "Optimization Hyperparameters" (linear

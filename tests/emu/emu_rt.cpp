@@ -387,6 +387,45 @@ void mfma_fn(void*) {
 }
 }  // namespace
 
+namespace {
+struct MfmaH16In {
+  f16x8_t a, b;
+  f32x16_t c;
+};
+void mfma_h16_fn(void*) {
+  float A[32][16], B[16][32], D[32][32];
+  for (int l = 0; l < 64; ++l) {
+    const MfmaH16In* p = (const MfmaH16In*)lane_in(l);
+    for (int s = 0; s < 8; ++s) {
+      A[l & 31][8 * (l >> 5) + s] = p ? (float)p->a[s] : 0.f;
+      B[8 * (l >> 5) + s][l & 31] = p ? (float)p->b[s] : 0.f;
+    }
+    for (int e = 0; e < 16; ++e) D[8 * (e >> 2) + 4 * (l >> 5) + (e & 3)][l & 31] = p ? p->c[e] : 0.f;
+  }
+  for (int i = 0; i < 32; ++i)
+    for (int k = 0; k < 16; ++k) {
+      const float a = A[i][k];
+      for (int j = 0; j < 32; ++j) D[i][j] = std::fma(a, B[k][j], D[i][j]);
+    }
+  for (int l = 0; l < 64; ++l) {
+    f32x16_t o;
+    for (int e = 0; e < 16; ++e) o[e] = D[8 * (e >> 2) + 4 * (l >> 5) + (e & 3)][l & 31];
+    std::memcpy(lane_out(l), &o, sizeof(o));
+  }
+}
+}  // namespace
+
+f32x16_t mfma_32x32x16_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
+  MfmaH16In in;
+  in.a = a;
+  in.b = b;
+  in.c = c;
+  void* r = wave_collective(6, &in, sizeof(in), mfma_h16_fn, nullptr);
+  f32x16_t o;
+  std::memcpy(&o, r, sizeof(o));
+  return o;
+}
+
 f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   MfmaIn in;
   in.a = a;

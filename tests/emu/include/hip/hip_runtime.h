@@ -12,6 +12,7 @@
 //  * v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 of A (k = 8*(l/32)
 //    .. +7) and column l%32 of B (same k); accumulator element e of lane l
 //    is D[8*(e/4) + 4*(l/32) + e%4][l%32].
+//  * v_mfma_f32_32x32x16_f16: as the bf16 instruction, with fp16 values.
 //  * v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and
 //    B[l/32][l%32]; the same accumulator layout.
 //  * ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
@@ -131,11 +132,13 @@ const void* lane_in(int lane);   // NULL for a lane that has exited
 void* lane_out(int lane);
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c);
 f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c);
+f32x16_t mfma_32x32x16_f16(f16x8_t a, f16x8_t b, f32x16_t c);
 v4s_t ds_read_tr16_b64(const void* lds_addr);
 
 struct Rsrc {
@@ -229,6 +232,7 @@ inline void __syncthreads() { ::emu::syncthreads(); }
 // ------------------------------------------------------------------ builtins
 #define __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, x, y, z) ::emu::mfma_32x32x16_bf16(a, b, c)
 #define __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, x, y, z) ::emu::mfma_32x32x2_f32(a, b, c)
+#define __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, x, y, z) ::emu::mfma_32x32x16_f16(a, b, c)
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16_b64((const void*)(p))
 #define __builtin_amdgcn_make_buffer_rsrc(b, s, n, f) ::emu::make_rsrc(b, s, n, f)
 #define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, sz, vo, so, of, ax) \

@@ -27,6 +27,7 @@ G124 = inputs.PRESETS["gpt2_124m"]
 G124U = inputs.PRESETS["gpt2_124m_v50257"]
 G124A = inputs.PRESETS["gpt2_124m_accum"]
 G124F = inputs.PRESETS["gpt2_124m_fp32"]
+SMALL_F16 = {**SMALL_BF16, "compute": "fp16"}
 
 
 # ---------------------------------------------------------------------------- small configurations
@@ -326,6 +327,59 @@ def generate_matches_oracle(be: Backend, preset: str, B: int = 2, T0: int = 7, T
     # (intervals ~2e-5 wide) a fair share of picks may then differ; a wrong
     # distribution would still match almost none.
     assert exact >= (0.9 if preset == "fp32" else 0.5) * B * (T - T0)
+
+
+def fp16_ragged_step(be: Backend):
+    """fp16 operands with dynamic loss scaling (scale 65536 at create) on the
+    ragged configuration: the bf16 tolerances apply (fp16 has more mantissa
+    bits, the loss scale keeps small gradients representable)."""
+    assert_bf16(*run_step(SMALL_F16, 3, 100, seed=1, data_seed=2, be=be))
+
+
+def fp16_loss_scaler(be: Backend):
+    """The dynamic loss scale: 65536 at create; an overflow (scale 2^40
+    makes the fp16 gradients non-finite) skips the step on the device
+    (parameters, moments and step count bitwise unchanged, norm reported as
+    +inf, status OK) and halves the scale; after `growth_interval` finite
+    steps the scale doubles; and two finite scales give the same update up
+    to fp16 rounding (scaling is divided out)."""
+    lc, oc, p = configs(SMALL_F16, 2, 32)
+    x, y = inputs.batch_from_stream(stream_for(p, 65, 3), 2, 32)
+    m = be.make(lc, 0)
+    assert m.loss_scale() == 65536.0
+    m.set_loss_scale(2.0 ** 40, 2000)
+    before = {n: v.clone() for n, v in m.state_dict().items() if n != "__step__"}
+    m.forward(be.dev(x), be.dev(y))
+    m.backward(1.0)
+    assert m.step(1e-3) == float("inf")
+    after = m.state_dict()
+    assert after["__step__"] == 0
+    for n in before:
+        assert torch.equal(before[n], after[n]), n
+    assert m.loss_scale() == 2.0 ** 39
+    m.set_loss_scale(256.0, 2)
+    norms = []
+    for k in range(3):
+        m.forward(be.dev(x), be.dev(y))
+        m.backward(1.0)
+        norms.append(m.step(1e-3))
+    assert all(np.isfinite(norms))
+    assert m.loss_scale() == 512.0 and m.step_count() == 3
+    m.check_arena()
+    m.close()
+    outs = []
+    for S in (256.0, 4096.0):
+        m = be.make(lc, 0)
+        m.set_loss_scale(S, 2000)
+        m.forward(be.dev(x), be.dev(y))
+        m.backward(1.0)
+        nrm = m.step(1e-3)
+        names = m.param_names()
+        outs.append((nrm, gpu_params(m, names)))
+        m.close()
+    assert abs(outs[0][0] - outs[1][0]) <= 1e-2 * outs[1][0]
+    for n in outs[0][1]:
+        assert np.abs(outs[0][1][n] - outs[1][1][n]).max() <= 2 * 1e-3 + 1e-6, n
 
 
 # ---------------------------------------------------------------------------- GPT-2 124M shapes

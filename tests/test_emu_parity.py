@@ -122,3 +122,11 @@ def test_emu_eval_loss_forward_only(preset):
 @pytest.mark.parametrize("preset", ["fp32", "bf16"])
 def test_emu_generate_matches_oracle(preset):
     cases.generate_matches_oracle(EMU, preset)
+
+
+def test_emu_fp16_ragged_step():
+    cases.fp16_ragged_step(EMU)
+
+
+def test_emu_fp16_loss_scaler():
+    cases.fp16_loss_scaler(EMU)

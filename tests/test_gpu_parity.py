@@ -70,3 +70,11 @@ def test_eval_loss_forward_only(preset):
 @pytest.mark.parametrize("preset", ["fp32", "bf16"])
 def test_generate_matches_oracle(preset):
     cases.generate_matches_oracle(GPU, preset)
+
+
+def test_fp16_ragged_step():
+    cases.fp16_ragged_step(GPU)
+
+
+def test_fp16_loss_scaler():
+    cases.fp16_loss_scaler(GPU)
