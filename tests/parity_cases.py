@@ -416,7 +416,8 @@ def _one_sequence_batches(x, y):
     return [(x[b:b + 1], y[b:b + 1]) for b in range(x.shape[0])]
 
 
-def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6e-4, n_layer=None):
+def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6e-4, n_layer=None,
+                        compute=None):
     """A whole step (forward, backward, clip, AdamW) of B sequences of T
     Zipf ids in ONE forward/backward of the library, against the oracle's
     step over the same B sequences taken as B one-sequence micro-batches at
@@ -424,9 +425,12 @@ def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6
     accumulation is linear; pinned on the CPU).  Loss 2e-2, per-tensor
     gradient cosine 0.999, post-AdamW rule."""
     over = {} if n_layer is None else {"n_layer": n_layer}
+    if compute:
+        over["compute"] = compute
     lc, oc, p = configs(preset, B, T, **over)
     x, y = inputs.batch_from_stream(stream_for(p, B * T + 1, 0), B, T)
-    say(f"[{be.name}] full step layers={p['n_layer']} V={p['vocab_size']}/{p['padded_vocab']} B={B} T={T}")
+    say(f"[{be.name}] full step layers={p['n_layer']} V={p['vocab_size']}/{p['padded_vocab']} B={B} T={T} "
+        f"{p['compute']}")
     m = be.make(lc, 0)
     loss = m.forward(be.dev(x), be.dev(y))
     per = m.view("losses")[:B * T].cpu().numpy()

@@ -64,3 +64,8 @@ def test_emu_generate_124m_width():
 @slow
 def test_emu_full_step_fp32_124m_width():
     cases.full_step_fp32_vs_oracle(EMU, 2, 64, n_layer=2)
+
+
+@slow
+def test_emu_full_step_fp16_124m_width():
+    cases.full_step_vs_oracle(EMU, cases.G124, 2, 64, n_layer=2, compute="fp16")

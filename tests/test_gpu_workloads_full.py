@@ -8,7 +8,8 @@
     the sum of the micro-steps' gradients;
   * sampling with the key/value cache at the 124M shape (4 sequences, a
     64-token prefix, 64 new tokens);
-  * the whole step in fp32 throughout (fp32 matrix-core GEMMs), B=4, T=1024.
+  * the whole step in fp32 throughout (fp32 matrix-core GEMMs), B=4, T=1024;
+  * the whole step with fp16 operands and dynamic loss scaling, B=4, T=1024.
 The oracle takes each batch as one-sequence micro-batches (exactly the same
 step by linearity of accumulation, pinned on the CPU), so it never holds a
 whole batch's logits.  Each test stays well under pytest's 900 s limit on the
@@ -43,3 +44,7 @@ def test_generate_124m_with_kv_cache():
 
 def test_full_step_fp32_124m():
     cases.full_step_fp32_vs_oracle(GPU, 4, 1024)
+
+
+def test_full_step_fp16_124m():
+    cases.full_step_vs_oracle(GPU, cases.G124, 4, 1024, compute="fp16")
