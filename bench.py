@@ -58,7 +58,9 @@ def class_work(p, B, T, n_params):
     per causal score (QK^T and PV) forward, twice that backward (recompute
     not credited).  LayerNorm forward (6C+8) and backward (14C+8) bytes per
     token over 2L+1 LayerNorms; cross-entropy (4 Vp + 8) bytes per token;
-    gradient norm 4 bytes and AdamW 30 bytes per parameter."""
+    gradient norm 4 bytes and AdamW 30 bytes per parameter; the transposed
+    weight copies 4 bytes (one 16-bit read, one write) per GEMM-weight
+    element."""
     L, C, H, Vp = p["n_layer"], p["n_embd"], p["n_head"], p["padded_vocab"]
     M = B * T
     hd = C // H
@@ -75,6 +77,7 @@ def class_work(p, B, T, n_params):
         "xent": ("hbm", M * (4 * Vp + 8), "byte"),
         "norm": ("hbm", 4 * n_params, "byte"),
         "adamw": ("hbm", 30 * n_params, "byte"),
+        "transpose": ("hbm", 4 * (Vp * C + L * 12 * C * C), "byte"),
     }
 
 

@@ -149,6 +149,9 @@ struct gpt2_ctx {
   uint16_t* shadow_t;              // transposed 16-bit copies of the GEMM weights
   std::vector<size_t> toff;        // element offset of each transposed copy (or -1)
   std::vector<int> tld;            // its row stride
+  std::vector<gk::TransposeJob> tjobs;  // one per transposed copy (host copy of the table)
+  gk::TransposeJob* tjobs_dev = nullptr;
+  int ttiles = 0;
   std::vector<float*> h, mean, rstd, lse;
   std::vector<void*> ln, qkv, att, fcu, fcg;
   void* logits;
@@ -260,6 +263,21 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     nt += (size_t)specs[j].cols * ld;
   }
   size_t o_sht = bf ? pl.raw(nt * 2 + 256, "transposed 16-bit weight copies") : 0;
+  std::vector<gk::TransposeJob> tjobs;
+  int ttiles = 0;
+  for (size_t j = 0; j < specs.size(); ++j) {
+    if (toff[j] == (size_t)-1) continue;
+    gk::TransposeJob jb;
+    jb.src = poff[j];
+    jb.dst = toff[j];
+    jb.R = (int32_t)specs[j].rows;
+    jb.C = (int32_t)specs[j].cols;
+    jb.ldt = tld[j];
+    jb.first_tile = ttiles;
+    ttiles += (int)(((specs[j].rows + 63) / 64) * ((specs[j].cols + 63) / 64));
+    tjobs.push_back(jb);
+  }
+  size_t o_tjobs = pl.raw(tjobs.size() * sizeof(gk::TransposeJob) + 8, "transpose job table");
   // tensor-table views of the flat arrays
   for (size_t j = 0; j < specs.size(); ++j) {
     auto& s = specs[j];
@@ -278,6 +296,17 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
       size_t es = k == 4 ? 2 : 4;
       t.offset = base[k] + poff[j] * es;
       t.bytes = s.numel() * es;
+      pl.out->push_back(t);
+    }
+    if (toff[j] != (size_t)-1) {  // transposed copy [in, ldt]: columns >= out are padding
+      t.name = "t16." + s.name;
+      t.kind = GPT2_K_SHADOW;
+      t.dtype = adt;
+      t.ndim = 2;
+      t.shape[0] = s.cols;
+      t.shape[1] = tld[j];
+      t.offset = o_sht + toff[j] * 2;
+      t.bytes = (size_t)s.cols * tld[j] * 2;
       pl.out->push_back(t);
     }
   }
@@ -340,6 +369,9 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     x->shadow_t = bf ? (uint16_t*)(a + o_sht) : nullptr;
     x->toff = toff;
     x->tld = tld;
+    x->tjobs = tjobs;
+    x->tjobs_dev = (gk::TransposeJob*)(a + o_tjobs);
+    x->ttiles = ttiles;
     x->nflat_t = nt;
     for (int k = 0; k <= 2 * L; ++k) {
       x->h.push_back((float*)(a + o_h[k]));
@@ -569,13 +601,7 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
 hipError_t refresh_transposed(gpt2_ctx* c) {
   if (!c->h16) return hipSuccess;
   Timed t(c, GPT2_T_TRANSPOSE);
-  for (size_t j = 0; j < c->specs.size(); ++j) {
-    if (c->toff[j] == (size_t)-1) continue;
-    const auto& sp = c->specs[j];
-    KCHK(gk::transpose_bf16(c->shadow + c->poff[j], (int)sp.rows, (int)sp.cols,
-                            c->shadow_t + c->toff[j], c->tld[j], c->st));
-  }
-  return hipSuccess;
+  return gk::transpose_jobs(c->shadow, c->shadow_t, c->tjobs_dev, (int)c->tjobs.size(), c->ttiles, c->st);
 }
 
 // The forward schedule over the ids already in c->tok ([B, T] packed):
@@ -740,6 +766,9 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
     if ((e = hipMemsetAsync(c->arena + g.offset, kGuardByte, kGuard, c->st))) return bail(e, "guards");
   if (c->h16 && (e = gk::to_h16(c->params, c->shadow, c->nflat, c->dt, c->st))) return bail(e, "16-bit copy");
   if (c->h16 && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
+  if (c->h16 && (e = hipMemcpyAsync(c->tjobs_dev, c->tjobs.data(), c->tjobs.size() * sizeof(gk::TransposeJob),
+                                    hipMemcpyHostToDevice, c->st)))
+    return bail(e, "transpose job table");
   if (c->ls) {  // dynamic loss scale and its step counter
     c->ls_staging[0] = 65536.f;
     c->ls_staging[1] = 0.f;

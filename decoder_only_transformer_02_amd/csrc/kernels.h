@@ -67,8 +67,16 @@ struct AdamChunk {
 hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow, int shadow_dt,
                  const AdamChunk* chunks, int nchunks, const float* scal, float lr, float beta1,
                  float beta2, float eps, float wd, hipStream_t st);
-// dst[c * ldt + r] = src[r * C + c] for a 16-bit [R, C] matrix (ldt even).
-hipError_t transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, int ldt, hipStream_t st);
+// Transposes of several 16-bit matrices in one launch: job j does
+// dst_base[dst + c * ldt + r] = src_base[src + r * C + c] (ldt even, element
+// offsets) over the 64 x 64 tiles [first_tile, first_tile + ceil(R/64)
+// ceil(C/64)); jobs ordered by first_tile, total_tiles the sum.
+struct TransposeJob {
+  uint64_t src, dst;
+  int32_t R, C, ldt, first_tile;
+};
+hipError_t transpose_jobs(const uint16_t* src_base, uint16_t* dst_base, const TransposeJob* jobs, int njobs,
+                          int total_tiles, hipStream_t st);
 // 16-bit copy (bf16 or fp16 per dt, round to nearest even) of n fp32 values.
 hipError_t to_h16(const float* x, uint16_t* y, size_t n, int dt, hipStream_t st);
 hipError_t fill_f32(float* x, size_t n, float v, hipStream_t st);

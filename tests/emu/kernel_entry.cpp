@@ -66,3 +66,9 @@ EMU_API int emu_colsum_parts(int M) { return gk::colsum_parts(M); }
 EMU_API int emu_colsum(const void* X, int dt, int M, int N, int ldx, float* db, float beta, float* part) {
   return (int)gk::colsum(X, dt, M, N, ldx, db, beta, part, nullptr);
 }
+
+// jobs: njobs x {src, dst (element offsets), R, C, ldt, first_tile} packed as
+// the library's TransposeJob.
+EMU_API int emu_transpose_jobs(const uint16_t* src, uint16_t* dst, const void* jobs, int njobs, int tiles) {
+  return (int)gk::transpose_jobs(src, dst, (const gk::TransposeJob*)jobs, njobs, tiles, nullptr);
+}

@@ -248,6 +248,36 @@ def arena_guard_detects_overrun(be: Backend):
     m.close()
 
 
+def transposed_copies_follow_weights(be: Backend, preset: str):
+    """Every transposed 16-bit weight copy is bitwise the transpose of the
+    weight's 16-bit copy, with zero padding columns, right after create and
+    after each optimizer step (one launch refreshes all of them)."""
+    p = SMALL_F16 if preset == "fp16" else SMALL_BF16
+    lc, oc, p = configs(p, 2, 24)
+    m = be.make(lc, 0)
+    names = [n[4:] for n in m.tensors if n.startswith("t16.")]
+    assert names and len(names) == 4 * p["n_layer"] + 1, names
+
+    def check():
+        for n in names:
+            w = m.view("bf16." + n).cpu()  # the 16-bit copy (bf16 or fp16)
+            t = m.view("t16." + n).cpu()
+            R, C = w.shape
+            assert t.shape[0] == C and t.shape[1] >= R and t.shape[1] % 64 == 0, n
+            assert torch.equal(t[:, :R].view(torch.int16), w.t().contiguous().view(torch.int16)), n
+            assert not t[:, R:].view(torch.int16).any(), n
+
+    check()
+    for k in range(2):
+        x, y = inputs.batch_from_stream(stream_for(p, 2 * 24 + 1, 11 + k), 2, 24)
+        m.forward(be.dev(x), be.dev(y))
+        m.backward(1.0)
+        m.step(1e-2)
+        check()
+    m.check_arena()
+    m.close()
+
+
 def eval_loss_forward_only(be: Backend, preset: str):
     """gpt2_eval_loss gives the forward's loss bitwise, leaves the raw logits
     in place (bitwise those of a forward without targets), does not arm

@@ -228,6 +228,37 @@ def test_emu_bias_column_sums(L):
     close(db, db0 + f64(X).sum(0), 1e-5, "column sums")
 
 
+def test_emu_transpose_jobs_ragged(L):
+    """One launch transposes several 16-bit matrices of odd and ragged shapes
+    (tiles split over rows and columns, a 1 x 1 job, odd R and C), each into
+    its own region with a padded row stride; bitwise against numpy, the
+    padding and the gaps between regions untouched."""
+    shapes = [(3, 5), (130, 67), (64, 64), (1, 1), (200, 129)]
+    rng = np.random.default_rng(7)
+    src_parts, jobs, so, do, tile = [], [], 0, 0, 0
+    for R, C in shapes:
+        src_parts.append(rng.integers(0, 65536, size=R * C, dtype=np.uint16))
+        ldt = (R + 63) // 64 * 64 + 2
+        jobs.append((so, do + 6, R, C, ldt, tile))
+        so += R * C
+        do += 6 + C * ldt + 10
+        tile += ((R + 63) // 64) * ((C + 63) // 64)
+    src = np.concatenate(src_parts)
+    dst = np.full(do, 0x5A5A, dtype=np.uint16)
+    table = np.zeros(len(jobs), dtype=[("src", "<u8"), ("dst", "<u8"), ("R", "<i4"), ("C", "<i4"),
+                                       ("ldt", "<i4"), ("first", "<i4")])
+    for i, j in enumerate(jobs):
+        table[i] = j
+    assert table.itemsize == 32
+    assert L.emu_transpose_jobs(ptr(src), ptr(dst), ptr(table), len(jobs), tile) == 0
+    want = np.full(do, 0x5A5A, dtype=np.uint16)
+    for (s0, d0, R, C, ldt, _), part in zip(jobs, src_parts):
+        blk = np.full((C, ldt), 0x5A5A, dtype=np.uint16)
+        blk[:, :R] = part.reshape(R, C).T
+        want[d0:d0 + C * ldt] = blk.ravel()
+    assert np.array_equal(dst, want)
+
+
 # ---------------------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("B,T,H", [(1, 1024, 2), (2, 100, 3)])

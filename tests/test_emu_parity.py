@@ -110,6 +110,11 @@ def test_emu_checkpoint_resume_bitwise(preset):
     cases.checkpoint_resume_bitwise(EMU, preset)
 
 
+@pytest.mark.parametrize("preset", ["bf16", "fp16"])
+def test_emu_transposed_copies_follow_weights(preset):
+    cases.transposed_copies_follow_weights(EMU, preset)
+
+
 def test_emu_arena_guard_detects_overrun():
     cases.arena_guard_detects_overrun(EMU)
 

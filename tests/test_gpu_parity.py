@@ -58,6 +58,11 @@ def test_checkpoint_resume_bitwise(preset):
     cases.checkpoint_resume_bitwise(GPU, preset)
 
 
+@pytest.mark.parametrize("preset", ["bf16", "fp16"])
+def test_transposed_copies_follow_weights(preset):
+    cases.transposed_copies_follow_weights(GPU, preset)
+
+
 def test_arena_guard_detects_overrun():
     cases.arena_guard_detects_overrun(GPU)
 
