@@ -7,7 +7,10 @@
 // head_dim 64, 16-bit operands (bf16 or fp16): matrix-core kernels.  Each
 // wave owns 32 queries (or
 // 32 keys in the dK/dV kernel) as the 32-wide MFMA column; K/V (or Q/dO)
-// tiles of 64 rows are staged in LDS and shared by the 4 waves of a block.
+// tiles of 64 rows are staged in LDS, double-buffered (one barrier per
+// tile), and shared by the 4 waves of a block.  Tiles keep the row-major
+// [row][d] layout; operands that need the contraction over rows (P V,
+// dS K, P^T dO, dS^T Q) are built with the gfx950 LDS transpose read.
 // Scores are formed transposed (S^T = K Q^T) so that a lane holds 16 scores
 // of one query: the online softmax needs one cross-lane exchange and the
 // probabilities feed the next MFMA straight from registers.  exp2 with the
@@ -23,18 +26,54 @@
 namespace gk {
 
 constexpr float LOG2E_F = 1.4426950408889634f;
-constexpr int ALD = 72;  // padded LDS row (16-bit elements)
+constexpr int TILE = 64 * 64;  // one LDS tile, 16-bit elements
+
+// LDS tiles are 64 rows of 64 16-bit values (128-byte rows, no padding);
+// the 16-byte chunk p of row r is stored at chunk p ^ rev3((r / 2) % 8).
+// With 64 banks of 4 bytes, row r covers the bank groups (4 banks each)
+// 8 (r % 2) + chunk, so
+//  * 16 consecutive rows reading (or writing) one chunk, 16 bytes each,
+//    hit 16 distinct groups: per row parity, rev3 takes 8 distinct values;
+//  * a transpose read of rows 4a .. 4a+3 by chunks 4c .. 4c+3 (the two
+//    16-lane groups that share a cycle) hits 16 distinct groups: rows 4a and
+//    4a+2 (and 4a+1, 4a+3) differ in bit 2 of their swizzle, which sends
+//    their chunk quartets to opposite halves of the row.
+__device__ __forceinline__ int rev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1); }
+__device__ __forceinline__ int sw_off(int r, int p) { return r * 64 + ((p ^ rev3((r >> 1) & 7)) << 3); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 template <typename TE>
 __device__ __forceinline__ uint4 ldg16(const TE* p) { return *(const uint4*)p; }
 
-// 8 values for the MFMA operand slots s = 0..7 gathered as keys
-// base + {0,1,2,3} and base + 8 + {0,1,2,3} from an LDS row (two 8-byte reads).
+// Row-major MFMA operand: lane l holds the 8 values of chunk p of tile row r.
 template <typename TE>
-__device__ __forceinline__ typename H16<TE>::v8 lds_two_runs(const uint16_t* row, int base) {
-  uint2 a = *(const uint2*)(row + base);
-  uint2 b = *(const uint2*)(row + base + 8);
-  return __builtin_bit_cast(typename H16<TE>::v8, make_uint4(a.x, a.y, b.x, b.y));
+__device__ __forceinline__ typename H16<TE>::v8 lds_row(const uint16_t* tile, int r, int p) {
+  return __builtin_bit_cast(typename H16<TE>::v8, *(const uint4*)(tile + sw_off(r, p)));
+}
+
+// Transposed MFMA operand: lane l serves column cbase + l % 32 of a tile
+// and its slots s = 0..7 hold rows rbase + {0,1,2,3} and rbase + 8 +
+// {0,1,2,3} (rbase is the lane's own, a multiple of 4).  Each
+// ds_read_b64_tr_b16 has the 16 lanes of a group read a 4-row x 16-column
+// block (lane 4j + c: row rbase + j, columns 4c .. 4c+3 of the group's 16)
+// and hands lane i the 4 rows of column i.
+template <typename TE>
+__device__ __forceinline__ typename H16<TE>::v8 lds_tr(const uint16_t* tile, int cbase, int rbase, int lane) {
+  const int q = lane & 15;
+  const int col = cbase + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+  v4s h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = rbase + 8 * hh + (q >> 2);
+    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + sw_off(r, col >> 3) + (col & 7)));
+  }
+  return __builtin_bit_cast(typename H16<TE>::v8,
+                            make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
+                                       __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
+                                       __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
+                                       __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]})));
 }
 
 // Pack accumulator values e = 8h .. 8h+7 of one 32x32 block to 16-bit slots.
@@ -70,37 +109,81 @@ struct Tile64 {
       v[i] = gr < T ? ldg16(base + (size_t)gr * ld + oct * 8) : make_uint4(0, 0, 0, 0);
     }
   }
-  // [row][col] layout
+  // swizzled [row][col] layout
   __device__ __forceinline__ void store(uint16_t* dn) const {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int c = threadIdx.x + i * 256;
       int row = c & 63, oct = c >> 6;
-      *(uint4*)(dn + row * ALD + oct * 8) = v[i];
-    }
-  }
-  // [col][row] layout
-  __device__ __forceinline__ void store_t(uint16_t* dt) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int c = threadIdx.x + i * 256;
-      int row = c & 63, oct = c >> 6;
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        dt[(oct * 8 + j) * ALD + row] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+      *(uint4*)(dn + sw_off(row, oct)) = v[i];
     }
   }
 };
 
 // ------------------------------------------------------------------ forward, hd = 64
+// One 64-key tile of the forward for one wave (32 queries from qw0, the
+// lane's query q): S^T = K Q^T from the row-major key tile, online-softmax
+// update of (m, l), O^T += V^T P^T with V^T from the transpose read.
+template <typename TE>
+__device__ __forceinline__ void attn_fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                              const typename H16<TE>::v8 (&qf)[4], f32x16 (&oacc)[2],
+                                              float& m_i, float& l_i, int k0, int qw0, int q, int T, float sl2,
+                                              int lane) {
+  typedef typename H16<TE>::v8 v8;
+  const int fr = lane & 31, g = lane >> 5;
+  f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) s[kb] = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s[kb]);
+  const bool diag = k0 + 63 > qw0;  // tile reaches past the wave's first query
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = s[kb][e] * sl2;
+      if (diag) {
+        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key > q || key >= T) v = -INFINITY;
+      }
+      s[kb][e] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m_i, mx);
+  const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+  float ps = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pv = __builtin_amdgcn_exp2f(s[kb][e] - m_new);
+      s[kb][e] = pv;
+      ps += pv;
+    }
+  l_i = l_i * alpha + ps;
+  m_i = m_new;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v8 pb = pack_slots<TE>(s[j >> 1], j & 1);
+    int kbase = (j >> 1) * 32 + (j & 1) * 16 + g * 4;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) oacc[db] = mfma(lds_tr<TE>(Vs, db * 32, kbase, lane), pb, oacc[db]);
+  }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(256) void k_attn_fwd64(const TE* __restrict__ qkv,
                                                     TE* __restrict__ out, float* __restrict__ lse,
                                                     int T, int H, float sl2) {
   typedef typename H16<TE>::v8 v8;
-  __shared__ uint16_t Ks[64 * ALD];
-  __shared__ uint16_t Vt[64 * ALD];
+  __shared__ uint16_t Ks[2][TILE];
+  __shared__ uint16_t Vs[2][TILE];
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // heavy blocks first
@@ -123,69 +206,32 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const TE* __restrict__ qkv,
   const int ntiles = qlast / 64 + 1;
   const int wq_hi = min(q0 + 32 * w + 31, T - 1);
 
+  // tile kt sits in buffer kt % 2; the registers carry tile kt + 1 from its
+  // global load (issued after the compute of tile kt - 1) to its LDS store
+  // (after the compute of tile kt), and the one barrier per tile orders
+  // that store both after every wave's reads of the buffer's previous tile
+  // and before the reads of the next iteration.
   Tile64 kt_r, vt_r;
   kt_r.load(kbase_p, ld, 0, T);
   vt_r.load(vbase_p, ld, 0, T);
+  kt_r.store(Ks[0]);
+  vt_r.store(Vs[0]);
+  if (ntiles > 1) {
+    kt_r.load(kbase_p, ld, 64, T);
+    vt_r.load(vbase_p, ld, 64, T);
+  }
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * 64;
-    __syncthreads();
-    kt_r.store(Ks);
-    vt_r.store_t(Vt);
-    __syncthreads();
+    const int k0 = kt * 64, cur = kt & 1;
+    if (k0 <= wq_hi) attn_fwd_tile<TE>(Ks[cur], Vs[cur], qf, oacc, m_i, l_i, k0, q0 + 32 * w, q, T, sl2, lane);
     if (kt + 1 < ntiles) {
-      kt_r.load(kbase_p, ld, k0 + 64, T);
-      vt_r.load(vbase_p, ld, k0 + 64, T);
-    }
-    if (k0 > wq_hi) continue;
-    f32x16 s[2] = {zero16(), zero16()};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
-        s[kb] = mfma(a, qf[ks], s[kb]);
+      kt_r.store(Ks[cur ^ 1]);
+      vt_r.store(Vs[cur ^ 1]);
+      if (kt + 2 < ntiles) {
+        kt_r.load(kbase_p, ld, k0 + 128, T);
+        vt_r.load(vbase_p, ld, k0 + 128, T);
       }
-    const bool diag = k0 + 63 > q0 + 32 * w;  // tile reaches past the wave's first query
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[kb][e] * sl2;
-        if (diag) {
-          int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (key > q || key >= T) v = -INFINITY;
-        }
-        s[kb][e] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pv = __builtin_amdgcn_exp2f(s[kb][e] - m_new);
-        s[kb][e] = pv;
-        ps += pv;
-      }
-    l_i = l_i * alpha + ps;
-    m_i = m_new;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v8 pb = pack_slots<TE>(s[j >> 1], j & 1);
-      int kbase = (j >> 1) * 32 + (j & 1) * 16 + g * 4;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        v8 a = lds_two_runs<TE>(Vt + (db * 32 + fr) * ALD, kbase);
-        oacc[db] = mfma(a, pb, oacc[db]);
-      }
+      __syncthreads();
     }
   }
   const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
@@ -251,6 +297,44 @@ __global__ __launch_bounds__(256) void k_attn_bwd_pre(const TA* __restrict__ o,
 }
 
 // ------------------------------------------------------------------ dQ, hd = 64
+// One 64-key tile of dQ for one wave: S^T = K Q^T and dP^T = V dO^T from
+// row-major tiles, P from the saved log-sum-exp, dS^T = P (dP - D), and
+// dQ^T += K^T dS^T with K^T from the transpose read.
+template <typename TE>
+__device__ __forceinline__ void attn_dq_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                             const typename H16<TE>::v8 (&qf)[4],
+                                             const typename H16<TE>::v8 (&dof)[4], f32x16 (&dq)[2], float lq,
+                                             float Dq, int k0, int qw0, int q, int T, float sl2, int lane) {
+  typedef typename H16<TE>::v8 v8;
+  const int fr = lane & 31, g = lane >> 5;
+  const bool diag = k0 + 63 > qw0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s);
+      dp = mfma(lds_row<TE>(Vs, kb * 32 + fr, 2 * ks + g), dof[ks], dp);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = __builtin_amdgcn_exp2f(s[e] * sl2 - lq);
+      if (diag) {
+        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key > q || key >= T) p = 0.f;
+      }
+      s[e] = p * (dp[e] - Dq);  // dS^T
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      v8 dsb = pack_slots<TE>(s, hh);
+      int kbase = kb * 32 + hh * 16 + g * 4;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) dq[db] = mfma(lds_tr<TE>(Ks, db * 32, kbase, lane), dsb, dq[db]);
+    }
+  }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
                                                    const TE* __restrict__ dout,
@@ -259,9 +343,8 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
                                                    TE* __restrict__ dqkv, int T, int H, float sl2,
                                                    float scale) {
   typedef typename H16<TE>::v8 v8;
-  __shared__ uint16_t Ks[64 * ALD];
-  __shared__ uint16_t Kt[64 * ALD];
-  __shared__ uint16_t Vs[64 * ALD];
+  __shared__ uint16_t Ks[2][TILE];
+  __shared__ uint16_t Vs[2][TILE];
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;
@@ -288,51 +371,28 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
   const int ntiles = qlast / 64 + 1;
   const int wq_hi = min(q0 + 32 * w + 31, T - 1);
 
+  // double-buffered tiles, one barrier per tile (as in the forward)
   Tile64 kr, vr;
   kr.load(kp, ld, 0, T);
   vr.load(vp, ld, 0, T);
+  kr.store(Ks[0]);
+  vr.store(Vs[0]);
+  if (ntiles > 1) {
+    kr.load(kp, ld, 64, T);
+    vr.load(vp, ld, 64, T);
+  }
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * 64;
-    __syncthreads();
-    kr.store(Ks);
-    kr.store_t(Kt);
-    vr.store(Vs);
-    __syncthreads();
+    const int k0 = kt * 64, cur = kt & 1;
+    if (k0 <= wq_hi) attn_dq_tile<TE>(Ks[cur], Vs[cur], qf, dof, dq, lq, Dq, k0, q0 + 32 * w, q, T, sl2, lane);
     if (kt + 1 < ntiles) {
-      kr.load(kp, ld, k0 + 64, T);
-      vr.load(vp, ld, k0 + 64, T);
-    }
-    if (k0 > wq_hi) continue;
-    const bool diag = k0 + 63 > q0 + 32 * w;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Ks + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
-        s = mfma(a, qf[ks], s);
-        v8 v = __builtin_bit_cast(v8, *(const uint4*)(Vs + (kb * 32 + fr) * ALD + ks * 16 + g * 8));
-        dp = mfma(v, dof[ks], dp);
+      kr.store(Ks[cur ^ 1]);
+      vr.store(Vs[cur ^ 1]);
+      if (kt + 2 < ntiles) {
+        kr.load(kp, ld, k0 + 128, T);
+        vr.load(vp, ld, k0 + 128, T);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(s[e] * sl2 - lq);
-        if (diag) {
-          int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-          if (key > q || key >= T) p = 0.f;
-        }
-        s[e] = p * (dp[e] - Dq);  // dS^T
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        v8 dsb = pack_slots<TE>(s, hh);
-        int kbase = kb * 32 + hh * 16 + g * 4;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          v8 a = lds_two_runs<TE>(Kt + (db * 32 + fr) * ALD, kbase);
-          dq[db] = mfma(a, dsb, dq[db]);
-        }
-      }
+      __syncthreads();
     }
   }
   if (q < T) {
@@ -349,6 +409,61 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
 }
 
 // ------------------------------------------------------------------ dK, dV, hd = 64
+// One 64-query tile of dK/dV for one wave (32 keys from wk_lo, the lane's
+// key): S and dP for the tile's queries x the wave's keys from row-major
+// tiles, P from the saved log-sum-exp, dS = P (dP - D); dV^T += dO^T P and
+// dK^T += Q^T dS with dO^T and Q^T from the transpose read.
+template <typename TE>
+__device__ __forceinline__ void attn_dkv_tile(const uint16_t* Qs, const uint16_t* Os, const float* Ls,
+                                              const float* Ds, const typename H16<TE>::v8 (&kf)[4],
+                                              const typename H16<TE>::v8 (&vf)[4], f32x16 (&dk)[2],
+                                              f32x16 (&dv)[2], int q0, int wk_lo, int key, int T, float sl2,
+                                              int lane) {
+  typedef typename H16<TE>::v8 v8;
+  const int fr = lane & 31, g = lane >> 5;
+  const bool diag = q0 < wk_lo + 31;  // some (q, key) pairs of the tile are masked
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    // S and dP for 32 queries x this wave's 32 keys:
+    // rows q = q0 + qb*32 + 8(e/4) + 4g + e%4, column key
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s = mfma(lds_row<TE>(Qs, qb * 32 + fr, 2 * ks + g), kf[ks], s);
+      dp = mfma(lds_row<TE>(Os, qb * 32 + fr, 2 * ks + g), vf[ks], dp);
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int ql0 = qb * 32 + e4 * 8 + g * 4;
+      const float4 L4 = *(const float4*)(Ls + ql0);
+      const float4 D4 = *(const float4*)(Ds + ql0);
+      const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+      for (int e1 = 0; e1 < 4; ++e1) {
+        const int e = e4 * 4 + e1;
+        float p = __builtin_amdgcn_exp2f(s[e] * sl2 - Lr[e1]);
+        if (diag) {
+          int qq = q0 + ql0 + e1;
+          if (key > qq || qq >= T) p = 0.f;
+        }
+        s[e] = p;
+        dp[e] = p * (dp[e] - Dr[e1]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      v8 pb = pack_slots<TE>(s, hh);
+      v8 dsb = pack_slots<TE>(dp, hh);
+      int qbase = qb * 32 + hh * 16 + g * 4;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        dv[db] = mfma(lds_tr<TE>(Os, db * 32, qbase, lane), pb, dv[db]);
+        dk[db] = mfma(lds_tr<TE>(Qs, db * 32, qbase, lane), dsb, dk[db]);
+      }
+    }
+  }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dkv64(const TE* __restrict__ qkv,
                                                     const TE* __restrict__ dout,
@@ -357,11 +472,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                     TE* __restrict__ dqkv, int T, int H, float sl2,
                                                     float scale) {
   typedef typename H16<TE>::v8 v8;
-  __shared__ uint16_t Qs[64 * ALD];
-  __shared__ uint16_t Qt[64 * ALD];
-  __shared__ uint16_t Os[64 * ALD];   // dO [q][d]
-  __shared__ uint16_t Ot[64 * ALD];   // dO^T [d][q]
-  __shared__ float Ls[64], Ds[64];
+  __shared__ uint16_t Qs[2][TILE];
+  __shared__ uint16_t Os[2][TILE];   // dO [q][d]
+  __shared__ float Ls[2][64], Ds[2][64];
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int k0 = blockIdx.x * 128;
@@ -396,65 +509,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       dr = qq < T ? Dv[(size_t)bh * T + qq] : 0.f;
     }
   };
-  load_q(qt0);
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int q0 = qt * 64;
-    __syncthreads();
-    qr.store(Qs);
-    qr.store_t(Qt);
-    orr.store(Os);
-    orr.store_t(Ot);
+  // double-buffered tiles, one barrier per tile (as in the forward)
+  auto store_q = [&](int buf) {
+    qr.store(Qs[buf]);
+    orr.store(Os[buf]);
     if (tid < 64) {
-      Ls[tid] = lr;
-      Ds[tid] = dr;
+      Ls[buf][tid] = lr;
+      Ds[buf][tid] = dr;
     }
-    __syncthreads();
-    if (qt + 1 < nqt) load_q(qt + 1);
-    if (q0 + 63 < wk_lo || wk_lo >= T) continue;
-    const bool diag = q0 < wk_lo + 31;  // some (q, key) pairs of the tile are masked
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S and dP for 32 queries x this wave's 32 keys:
-      // rows q = q0 + qb*32 + 8(e/4) + 4g + e%4, column key
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8 a = __builtin_bit_cast(v8, *(const uint4*)(Qs + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
-        s = mfma(a, kf[ks], s);
-        v8 o = __builtin_bit_cast(v8, *(const uint4*)(Os + (qb * 32 + fr) * ALD + ks * 16 + g * 8));
-        dp = mfma(o, vf[ks], dp);
-      }
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int ql0 = qb * 32 + e4 * 8 + g * 4;
-        const float4 L4 = *(const float4*)(Ls + ql0);
-        const float4 D4 = *(const float4*)(Ds + ql0);
-        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-        for (int e1 = 0; e1 < 4; ++e1) {
-          const int e = e4 * 4 + e1;
-          float p = __builtin_amdgcn_exp2f(s[e] * sl2 - Lr[e1]);
-          if (diag) {
-            int qq = q0 + ql0 + e1;
-            if (key > qq || qq >= T) p = 0.f;
-          }
-          s[e] = p;
-          dp[e] = p * (dp[e] - Dr[e1]);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        v8 pb = pack_slots<TE>(s, hh);
-        v8 dsb = pack_slots<TE>(dp, hh);
-        int qbase = qb * 32 + hh * 16 + g * 4;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          v8 ao = lds_two_runs<TE>(Ot + (db * 32 + fr) * ALD, qbase);
-          dv[db] = mfma(ao, pb, dv[db]);
-          v8 aq = lds_two_runs<TE>(Qt + (db * 32 + fr) * ALD, qbase);
-          dk[db] = mfma(aq, dsb, dk[db]);
-        }
-      }
+  };
+  load_q(qt0);
+  store_q(0);
+  if (qt0 + 1 < nqt) load_q(qt0 + 1);
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int q0 = qt * 64, cur = (qt - qt0) & 1;
+    if (q0 + 63 >= wk_lo && wk_lo < T)
+      attn_dkv_tile<TE>(Qs[cur], Os[cur], Ls[cur], Ds[cur], kf, vf, dk, dv, q0, wk_lo, key, T, sl2, lane);
+    if (qt + 1 < nqt) {
+      store_q(cur ^ 1);
+      if (qt + 2 < nqt) load_q(qt + 2);
+      __syncthreads();
     }
   }
   if (key < T) {

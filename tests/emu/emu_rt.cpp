@@ -12,6 +12,7 @@
 #include <condition_variable>
 #include <deque>
 #include <mutex>
+#include <pthread.h>
 #include <string>
 #include <thread>
 #include <vector>
@@ -19,6 +20,7 @@
 #if defined(__has_feature)
 #if __has_feature(address_sanitizer)
 #define EMU_ASAN 1
+#include <sanitizer/asan_interface.h>
 #include <sanitizer/common_interface_defs.h>
 #endif
 #endif
@@ -152,6 +154,13 @@ void run_block() {
     f.wave = i >> 6;
     f.tid = dim3(i % W->bdim.x, (i / W->bdim.x) % W->bdim.y, i / (W->bdim.x * W->bdim.y));
     f.state = RUN;
+#ifdef EMU_ASAN
+    // A fiber stack is reused block after block, and frames that never
+    // returned (a finished fiber's last switch) leave poisoned redzones in
+    // its shadow, which later kernels' stack data can land on: start every
+    // fiber with a clean shadow, as for any reused stack.
+    __asan_unpoison_memory_region(W->stacks[i], STACK);
+#endif
     uintptr_t top = ((uintptr_t)(W->stacks[i] + STACK)) & ~(uintptr_t)15;
     void** sp = (void**)top - 8;
     for (int k = 0; k < 6; ++k) sp[k] = nullptr;
@@ -273,6 +282,15 @@ Pool* pool() {
     if (const char* e = std::getenv("EMU_THREADS")) n = std::atoi(e);
     if (n < 1) n = 1;
     if (n > 64) n = 64;
+    // Every kernel's LDS arrays are thread_local in this build, and glibc
+    // carves static TLS out of each thread's stack: give the workers room
+    // (the sanitizer builds' larger frames overflowed the default).
+    pthread_attr_t attr;
+    if (pthread_getattr_default_np(&attr) == 0) {
+      pthread_attr_setstacksize(&attr, (size_t)64 << 20);
+      pthread_setattr_default_np(&attr);
+      pthread_attr_destroy(&attr);
+    }
     q->start(n);
     return q;
   }();

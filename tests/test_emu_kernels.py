@@ -261,15 +261,20 @@ def test_emu_transpose_jobs_ragged(L):
 
 # ---------------------------------------------------------------------------- attention
 
-@pytest.mark.parametrize("B,T,H", [(1, 1024, 2), (2, 100, 3)])
-def test_emu_flash_attention_forward_backward(L, B, T, H):
+@pytest.mark.parametrize("B,T,H,dt", [(1, 1024, 2, 1), (2, 100, 3, 1), (1, 37, 1, 2), (2, 193, 2, 2)])
+def test_emu_flash_attention_forward_backward(L, B, T, H, dt):
+    """Matrix-core attention (head size 64) against the oracle: a full 1024
+    sequence, ragged lengths that end mid-tile, a single partial tile and an
+    odd number of tiles (both LDS buffers, either parity at the end), bf16
+    (dt 1) and fp16 (dt 2)."""
     hd = 64
     C = H * hd
+    tt = torch.bfloat16 if dt == 1 else torch.float16
     rng = np.random.default_rng(T + H)
-    qkv = bf16(rng.standard_normal((B * T, 3 * C)))
-    o = torch.zeros((B * T, C), dtype=torch.bfloat16)
+    qkv = torch.from_numpy(rng.standard_normal((B * T, 3 * C)).astype(np.float32)).to(tt)
+    o = torch.zeros((B * T, C), dtype=tt)
     lse = np.zeros(B * H * T, np.float32)
-    assert L.emu_attn_fwd(ptr(qkv), ptr(o), ptr(lse), B, T, H, hd, 1) == 0
+    assert L.emu_attn_fwd(ptr(qkv), ptr(o), ptr(lse), B, T, H, hd, dt) == 0
     q64 = f64(qkv).reshape(B, T, 3, H, hd).transpose(2, 0, 3, 1, 4)  # [3, B, H, T, hd]
     q, k, v = q64[0], q64[1], q64[2]
     oref = O.causal_attention_fwd(q, k, v, np.float64)
@@ -279,10 +284,10 @@ def test_emu_flash_attention_forward_backward(L, B, T, H):
     s[..., np.triu(np.ones((T, T), bool), 1)] = -np.inf
     lse_ref = (np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1)) / np.log(2.0)
     close(lse.reshape(B, H, T), lse_ref, 1e-5, "lse (log2)")
-    dout = bf16(rng.standard_normal((B * T, C)))
-    dqkv = torch.zeros((B * T, 3 * C), dtype=torch.bfloat16)
+    dout = torch.from_numpy(rng.standard_normal((B * T, C)).astype(np.float32)).to(tt)
+    dqkv = torch.zeros((B * T, 3 * C), dtype=tt)
     ws = np.zeros(L.emu_attn_bwd_ws(B, T, H), np.float32)
-    assert L.emu_attn_bwd(ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws), B, T, H, hd, 1) == 0
+    assert L.emu_attn_bwd(ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws), B, T, H, hd, dt) == 0
     do = f64(dout).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
     dq, dk, dv = O.causal_attention_bwd(q, k, v, og, do, np.float64)
     got = f64(dqkv).reshape(B, T, 3, H, hd).transpose(2, 0, 3, 1, 4)
