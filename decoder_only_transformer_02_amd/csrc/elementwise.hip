@@ -12,13 +12,24 @@ namespace gk {
 
 // ------------------------------------------------------------------ helpers
 template <typename T> struct Vec4;
+// Raw / load_raw / cvt split a load from its conversion, so a load can be
+// issued ahead (a prefetch) without waiting for its data.
 template <> struct Vec4<float> {
+  typedef float4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ float4 cvt(Raw u) { return u; }
   static __device__ __forceinline__ float4 load(const float* p) { return *(const float4*)p; }
   static __device__ __forceinline__ void store(float* p, float a, float b, float c, float d) {
     *(float4*)p = make_float4(a, b, c, d);
   }
 };
 template <> struct Vec4<bf16> {
+  typedef uint2 Raw;
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ float4 cvt(Raw u) {
+    return make_float4(bfbits2f(u.x & 0xffffu), bfbits2f(u.x >> 16), bfbits2f(u.y & 0xffffu),
+                       bfbits2f(u.y >> 16));
+  }
   static __device__ __forceinline__ float4 load(const bf16* p) {
     uint2 u = *(const uint2*)p;
     return make_float4(bfbits2f(u.x & 0xffffu), bfbits2f(u.x >> 16), bfbits2f(u.y & 0xffffu),
@@ -29,6 +40,11 @@ template <> struct Vec4<bf16> {
   }
 };
 template <> struct Vec4<f16> {
+  typedef uint2 Raw;
+  static __device__ __forceinline__ Raw load_raw(const f16* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ float4 cvt(Raw u) {
+    return make_float4(H16<f16>::lo(u.x), H16<f16>::hi(u.x), H16<f16>::lo(u.y), H16<f16>::hi(u.y));
+  }
   static __device__ __forceinline__ float4 load(const f16* p) {
     uint2 u = *(const uint2*)p;
     return make_float4(H16<f16>::lo(u.x), H16<f16>::hi(u.x), H16<f16>::lo(u.y), H16<f16>::hi(u.y));
@@ -75,60 +91,77 @@ hipError_t embed_fwd(const int32_t* tok, const float* wte, const float* wpe, flo
 
 // ------------------------------------------------------------------ LayerNorm forward
 // y = (x - mean) * rstd * w + b, biased variance, one wave per row.  The row
-// stays in registers (NV float4 per lane, C <= 256 * NV).
+// stays in registers (NV float4 per lane, C <= 256 * NV).  Each wave walks
+// the rows wave_id, wave_id + nwaves, ... with w and b held in registers
+// and the next row's loads issued before the current row's reductions.
+constexpr int LN_FWD_BLOCKS = 1024;
+
 template <typename TO, int NV>
 __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
                                                 const float* __restrict__ w,
                                                 const float* __restrict__ b, TO* __restrict__ y,
                                                 float* __restrict__ mean, float* __restrict__ rstd,
                                                 int M, int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x * 4;
   int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
   if (row >= M) return;
-  const float* xr = x + (size_t)row * C;
-  float4 v[NV];
-  float s = 0.f;
+  float4 ww[NV], bb[NV], v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int c = (lane + i * 64) * 4;
-    if (c < C) {
-      v[i] = *(const float4*)(xr + c);
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    } else {
-      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    ww[i] = c < C ? *(const float4*)(w + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    bb[i] = c < C ? *(const float4*)(b + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = c < C ? *(const float4*)(x + (size_t)row * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float mu = wave_sum(s) / (float)C;
-  float q = 0.f;
+  const float invC = 1.0f / (float)C;
+  for (; row < M; row += stride) {
+    const bool more = row + stride < M;
+    float4 vn[NV];
+    if (more) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int c = (lane + i * 64) * 4;
-    if (c < C) {
-      float a0 = v[i].x - mu, a1 = v[i].y - mu, a2 = v[i].z - mu, a3 = v[i].w - mu;
-      q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+      for (int i = 0; i < NV; ++i) {
+        int c = (lane + i * 64) * 4;
+        vn[i] = c < C ? *(const float4*)(x + (size_t)(row + stride) * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-  }
-  float rs = rsqrtf(wave_sum(q) / (float)C + eps);
-  TO* yr = y + (size_t)row * C;
+    float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int c = (lane + i * 64) * 4;
-    if (c < C) {
-      float4 ww = *(const float4*)(w + c), bb = *(const float4*)(b + c);
-      Vec4<TO>::store(yr + c, (v[i].x - mu) * rs * ww.x + bb.x, (v[i].y - mu) * rs * ww.y + bb.y,
-                      (v[i].z - mu) * rs * ww.z + bb.z, (v[i].w - mu) * rs * ww.w + bb.w);
+    for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mu = wave_sum(s) * invC;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int c = (lane + i * 64) * 4;
+      if (c < C) {
+        float a0 = v[i].x - mu, a1 = v[i].y - mu, a2 = v[i].z - mu, a3 = v[i].w - mu;
+        q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+      }
     }
-  }
-  if (lane == 0) {
-    mean[row] = mu;
-    rstd[row] = rs;
+    const float rs = rsqrtf(wave_sum(q) * invC + eps);
+    TO* yr = y + (size_t)row * C;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int c = (lane + i * 64) * 4;
+      if (c < C)
+        Vec4<TO>::store(yr + c, (v[i].x - mu) * rs * ww[i].x + bb[i].x, (v[i].y - mu) * rs * ww[i].y + bb[i].y,
+                        (v[i].z - mu) * rs * ww[i].z + bb[i].z, (v[i].w - mu) * rs * ww[i].w + bb[i].w);
+    }
+    if (lane == 0) {
+      mean[row] = mu;
+      rstd[row] = rs;
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = vn[i];
+    }
   }
 }
 
 hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, int dt, float* mean,
                   float* rstd, int M, int C, float eps, hipStream_t st) {
   if (C % 4 || C > 1024) return hipErrorInvalidValue;
-  int g = cdiv(M, 4);
+  int g = min(cdiv(M, 4), LN_FWD_BLOCKS);
   if (dt == ACT_BF16)
     k_ln_fwd<bf16, 4><<<g, 256, 0, st>>>(x, w, b, (bf16*)y, mean, rstd, M, C, eps);
   else if (dt == ACT_F16)
@@ -169,18 +202,51 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
     dba[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const float invC = 1.0f / (float)C;
-  for (int row = r0 + wv; row < r1; row += 4) {
-    float mu = mean[row], rs = rstd[row];
-    const float* xr = x + (size_t)row * C;
-    const TA* dyr = dy + (size_t)row * C;
+  typedef typename Vec4<TA>::Raw Raw;
+  // The wave's rows are row, row + 4, ...: the next row's x, dy, mean and
+  // rstd are loaded before the current row's reductions, so each wave keeps
+  // two rows of loads in flight.
+  float4 xc[NV];
+  Raw dc[NV];
+  float mu = 0.f, rs = 0.f;
+  auto load_row = [&](int r, float4 (&xo)[NV], Raw (&d_o)[NV], float& mu_o, float& rs_o) {
+    mu_o = mean[r];
+    rs_o = rstd[r];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int c = (lane + i * 64) * 4;
+      if (c < C) {
+        xo[i] = *(const float4*)(x + (size_t)r * C + c);
+        d_o[i] = Vec4<TA>::load_raw(dy + (size_t)r * C + c);
+      }
+    }
+  };
+  int row = r0 + wv;
+  if (row < r1) load_row(row, xc, dc, mu, rs);
+  for (; row < r1; row += 4) {
+    const bool more = row + 4 < r1;
+    float4 xn[NV];
+    Raw dn[NV];
+    float mun = 0.f, rsn = 0.f;
+    if (more) load_row(row + 4, xn, dn, mun, rsn);
+    float* dr = dres + (size_t)row * C;
+    TA* da = dres_act + (size_t)row * C;
+    float4 prev[NV];
+    if (accum) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        int c = (lane + i * 64) * 4;
+        if (c < C) prev[i] = *(const float4*)(dr + c);
+      }
+    }
     float4 xh[NV], gg[NV];
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
       if (c < C) {
-        float4 xv = *(const float4*)(xr + c);
-        float4 d = Vec4<TA>::load(dyr + c);
+        const float4 xv = xc[i];
+        const float4 d = Vec4<TA>::cvt(dc[i]);
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
         gg[i] = make_float4(d.x * wr[i].x, d.y * wr[i].y, d.z * wr[i].z, d.w * wr[i].w);
         sg += (gg[i].x + gg[i].y) + (gg[i].z + gg[i].w);
@@ -191,8 +257,6 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
       }
     }
     float mg = wave_sum(sg) * invC, mgx = wave_sum(sgx) * invC;
-    float* dr = dres + (size_t)row * C;
-    TA* da = dres_act + (size_t)row * C;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
@@ -200,12 +264,20 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
         float4 o = make_float4(rs * (gg[i].x - mg - xh[i].x * mgx), rs * (gg[i].y - mg - xh[i].y * mgx),
                                rs * (gg[i].z - mg - xh[i].z * mgx), rs * (gg[i].w - mg - xh[i].w * mgx));
         if (accum) {
-          float4 p = *(const float4*)(dr + c);
-          o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
+          o.x += prev[i].x; o.y += prev[i].y; o.z += prev[i].z; o.w += prev[i].w;
         }
         *(float4*)(dr + c) = o;
         Vec4<TA>::store(da + c, o.x, o.y, o.z, o.w);
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        xc[i] = xn[i];
+        dc[i] = dn[i];
+      }
+      mu = mun;
+      rs = rsn;
     }
   }
 #pragma unroll
@@ -424,8 +496,52 @@ __device__ __forceinline__ uint4 chunk_pack<f16>(const float* f) {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// A chunk of -inf values (the padding of a row past its V logits: it drops
+// out of the max and the sum, and its gradient comes out as exp2(-inf) = 0).
+template <typename T>
+__device__ __forceinline__ uint4 chunk_neginf();
+template <>
+__device__ __forceinline__ uint4 chunk_neginf<float>() {
+  return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+}
+template <>
+__device__ __forceinline__ uint4 chunk_neginf<bf16>() {
+  return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+}
+template <>
+__device__ __forceinline__ uint4 chunk_neginf<f16>() {
+  return make_uint4(0xfc00fc00u, 0xfc00fc00u, 0xfc00fc00u, 0xfc00fc00u);
+}
+
+// u with its elements n .. E-1 replaced by -inf (all of them for n <= 0).
+template <typename T>
+__device__ __forceinline__ uint4 chunk_keep(uint4 u, int n) {
+  constexpr int E = Chunk16<T>::E;
+  const uint4 ninf = chunk_neginf<T>();
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const uint32_t m[4] = {ninf.x, ninf.y, ninf.z, ninf.w};
+  constexpr int PW = E / 4;  // elements per 32-bit word
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < PW; ++h)
+      if (i * PW + h >= n) {
+        const uint32_t mask = PW == 1 ? 0xffffffffu : (h ? 0xffff0000u : 0x0000ffffu);
+        w[i] = (w[i] & ~mask) | (m[i] & mask);
+      }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // DS: the gradient scale is also multiplied by *dev_scale (the dynamic
 // loss scale of the fp16 workload, which lives on the device).
+//
+// The element loops carry no per-element tests: the one chunk that
+// straddles V is padded with -inf at its load and chunks past V are all
+// -inf, so the max, the sum and the gradient need no bounds checks; the
+// target logit is read from the registers of the thread that holds it, and
+// the "- 1" of the target's gradient is written by that thread as one
+// element after its chunk store (same thread, same address: the later
+// store wins).
 template <typename T, int NCH, bool DS>
 __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, int V, int vt,
                                               const int32_t* __restrict__ tgt,
@@ -433,6 +549,7 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
                                               int want_grad, int* flag, const float* dev_scale) {
   constexpr int E = Chunk16<T>::E;
   __shared__ float sh[4];
+  __shared__ float sh_zy;
   int row = blockIdx.x;
   T* z = logits + (size_t)row * ld;
   int y = tgt[row];
@@ -440,62 +557,48 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
     if (threadIdx.x == 0) atomicOr(flag, FLAG_TARGET);
     y = y < 0 ? 0 : vt - 1;
   }
-  // The target logit is taken from the registers of the thread that loaded
-  // it (a separate global read could still be in flight when another wave
-  // overwrites the row with the gradient).
-  __shared__ float sh_zy;
+  const int ych = y / E;
   uint4 buf[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int e0 = (threadIdx.x + k * 256) * E;
+    buf[k] = e0 < ld ? *(const uint4*)(z + e0) : chunk_neginf<T>();
+    if (e0 + E > V) buf[k] = chunk_keep<T>(buf[k], V - e0);  // n <= 0: all -inf
+  }
+#pragma unroll
+  for (int k = 0; k < NCH; ++k)
+    if ((int)threadIdx.x + k * 256 == ych) sh_zy = chunk_elem<T>(buf[k], y - ych * E);
   float mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    int e0 = (threadIdx.x + k * 256) * E;
-    if (e0 < V) {
-      buf[k] = *(const uint4*)(z + e0);
+  for (int k = 0; k < NCH; ++k)
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        float v = chunk_elem<T>(buf[k], j);
-        if (e0 + j < V) mx = fmaxf(mx, v);
-        if (e0 + j == y) sh_zy = v;
-      }
-    }
-  }
+    for (int j = 0; j < E; ++j) mx = fmaxf(mx, chunk_elem<T>(buf[k], j));
   mx = block_reduce_max(mx, sh);
   const float zy = sh_zy;
+  const float mx2 = mx * LOG2E;
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    int e0 = (threadIdx.x + k * 256) * E;
-    if (e0 < V) {
+  for (int k = 0; k < NCH; ++k)
 #pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e0 + j < V) s += __builtin_amdgcn_exp2f((chunk_elem<T>(buf[k], j) - mx) * LOG2E);
-    }
-  }
+    for (int j = 0; j < E; ++j) s += __builtin_amdgcn_exp2f(fmaf(chunk_elem<T>(buf[k], j), LOG2E, -mx2));
   s = block_reduce_sum(s, sh);
   float lse = mx + __logf(s);
   if (threadIdx.x == 0) losses[row] = lse - zy;
   if (!want_grad) return;
   if constexpr (DS) scale *= dev_scale[0];
-  float lse2 = lse * LOG2E;
+  const float lse2 = lse * LOG2E;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
-    int e0 = (threadIdx.x + k * 256) * E;
+    const int e0 = (threadIdx.x + k * 256) * E;
     if (e0 < ld) {
       float f[E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        int e = e0 + j;
-        float g = 0.f;
-        if (e < V) {
-          g = __builtin_amdgcn_exp2f(chunk_elem<T>(buf[k], j) * LOG2E - lse2);
-          if (e == y) g -= 1.0f;
-          g *= scale;
-        }
-        f[j] = g;
-      }
+      for (int j = 0; j < E; ++j) f[j] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<T>(buf[k], j), LOG2E, -lse2)) * scale;
       *(uint4*)(z + e0) = chunk_pack<T>(f);
     }
   }
+  if ((int)threadIdx.x == ych % 256)
+    z[y] = from_f<T>((__builtin_amdgcn_exp2f(fmaf(zy, LOG2E, -lse2)) - 1.0f) * scale);
 }
 
 // Streaming variant (row too long for registers): three passes over HBM.
@@ -567,6 +670,7 @@ static hipError_t xent_t(T* logits, int ld, int V, int vt, const int32_t* tgt, f
 
 hipError_t xent(void* logits, int dt, int ld, int V, int vt, const int32_t* tgt, float* losses, float scale,
                 bool want_grad, int M, int* flag, const float* dev_scale, hipStream_t st) {
+  if (V < 1 || V > ld || vt < 1 || vt > V) return hipErrorInvalidValue;
   if (dt == ACT_F16) {
     if (ld % 8) return hipErrorInvalidValue;
     if (dev_scale)
@@ -606,50 +710,77 @@ hipError_t loss_reduce(const float* losses, int M, float* loss_out, int* flag, h
 // ------------------------------------------------------------------ embedding backward
 // Tied embedding ("parameter sharing wte and lm_head"): dwte[id] gains the
 // sum of the residual-gradient rows of every position holding id.  The
-// positions are sorted by (id, position) with a bitonic sort in LDS, then
-// summed per id in sorted order: each chunk of 32 sorted entries sums its
-// runs; runs that cross chunk borders are combined by a second kernel in
-// chunk order.  No atomics, so the result is deterministic.
-constexpr int SORT_MAX = 32768;  // positions per call (keys: id << 15 | pos)
+// positions are sorted by (id, position) as 32-bit keys id << 15 | pos,
+// then summed per id in sorted order: each chunk of 32 sorted entries sums
+// its runs; runs that cross chunk borders are combined by a second kernel
+// in chunk order.  No atomics, so the result is deterministic.
+//
+// The sort runs on the whole chip: blocks of 512 threads sort runs of 1024
+// keys with a bitonic network in LDS, then merge passes double the run
+// length until one run is left.  A merge pass places every key at its
+// index within its run plus the number of keys of the partner run below it
+// (a binary search; keys are distinct since positions are), so it needs no
+// partitioning step and every thread works independently.
+constexpr int SORT_MAX = 32768;  // positions per call (15 position bits)
+constexpr int SORT_RUN = 1024;   // keys per block in the first stage
 constexpr int SEG = 32;
 
 size_t embed_bwd_workspace(int M, int C) {
   size_t nch = (size_t)cdiv(M, SEG);
-  return (size_t)SORT_MAX * 4 + 2 * nch * (size_t)C * 4 + 256;
+  size_t mr = (size_t)cdiv(M, SORT_RUN) * SORT_RUN;
+  return 2 * mr * 4 + 2 * nch * (size_t)C * 4 + 256;
 }
 
-__global__ __launch_bounds__(1024) void k_sort_keys(const int32_t* __restrict__ tok, int M, int V,
-                                                    uint32_t* __restrict__ out) {
-  extern __shared__ uint32_t sk[];
-  int N = 1;
-  while (N < M) N <<= 1;
-  for (int i = threadIdx.x; i < N; i += 1024) {
-    uint32_t key = 0xffffffffu;
-    if (i < M) {
-      int id = tok[i];
+__global__ __launch_bounds__(512) void k_sort_runs(const int32_t* __restrict__ tok, int M, int V,
+                                                   uint32_t* __restrict__ out) {
+  __shared__ uint32_t sk[SORT_RUN];
+  const int base = blockIdx.x * SORT_RUN;
+  for (int i = threadIdx.x; i < SORT_RUN; i += 512) {
+    uint32_t key = 0xffffffffu;  // above every real key: ids < 65536, positions < 32768
+    if (base + i < M) {
+      int id = tok[base + i];
       id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-      key = ((uint32_t)id << 15) | (uint32_t)i;
+      key = ((uint32_t)id << 15) | (uint32_t)(base + i);
     }
     sk[i] = key;
   }
   __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
+  const int t = threadIdx.x;
+  for (int k = 2; k <= SORT_RUN; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < N; i += 1024) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint32_t a = sk[i], b = sk[ixj];
-          bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            sk[i] = b;
-            sk[ixj] = a;
-          }
-        }
+      const int i = (t / j) * 2 * j + (t % j), ixj = i + j;  // pair t of this stage
+      const uint32_t a = sk[i], b = sk[ixj];
+      const bool up = (i & k) == 0;
+      if ((a > b) == up) {
+        sk[i] = b;
+        sk[ixj] = a;
       }
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < M; i += 1024) out[i] = sk[i];
+  for (int i = threadIdx.x; i < SORT_RUN && base + i < M; i += 512) out[base + i] = sk[i];
+}
+
+// Sorted runs [a0, a0 + L) and [a0 + L, a0 + 2L) of `in` (clipped at M)
+// merged into out[a0 ..): key x of one run lands at its offset in its run
+// plus the count of keys below x in the other run.
+__global__ __launch_bounds__(256) void k_merge_runs(const uint32_t* __restrict__ in, uint32_t* __restrict__ out,
+                                                    int M, int L) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M) return;
+  const uint32_t x = in[i];
+  const int a0 = (i / (2 * L)) * 2 * L;
+  const bool first = i < a0 + L;
+  const int o0 = first ? a0 + L : a0;               // the other run
+  const int o1 = first ? min(a0 + 2 * L, M) : a0 + L;
+  int lo = o0, hi = o1;                              // first index in [o0, o1) with key > x
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (in[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  const int own = first ? i - a0 : i - (a0 + L);
+  out[a0 + own + (lo - o0)] = x;
 }
 
 __device__ __forceinline__ int key_id(uint32_t k) { return (int)(k >> 15); }
@@ -730,19 +861,17 @@ __global__ __launch_bounds__(256) void k_dwpe(const float* __restrict__ dh, floa
 hipError_t embed_bwd(const int32_t* tok, const float* dh, float* dwte, float* dwpe, int B, int T,
                      int C, int V, int block_size, float beta, void* ws, hipStream_t st) {
   int M = B * T;
-  if (M > SORT_MAX || V > 65536) return hipErrorInvalidValue;
-  uint32_t* keys = (uint32_t*)ws;
+  if (M < 1 || M > SORT_MAX || V > 65536) return hipErrorInvalidValue;
+  const size_t mr = (size_t)cdiv(M, SORT_RUN) * SORT_RUN;
+  uint32_t* kb[2] = {(uint32_t*)ws, (uint32_t*)ws + mr};
   int nch = cdiv(M, SEG);
-  float* pfirst = (float*)((char*)ws + (size_t)SORT_MAX * 4);
+  float* pfirst = (float*)(kb[1] + mr);
   float* plast = pfirst + (size_t)nch * C;
-  int N = 1;
-  while (N < M) N <<= 1;
-  if ((size_t)N * 4 > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_sort_keys,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, N * 4);
-    if (e != hipSuccess) return e;
-  }
-  k_sort_keys<<<1, 1024, (size_t)N * 4, st>>>(tok, M, V, keys);
+  k_sort_runs<<<cdiv(M, SORT_RUN), 512, 0, st>>>(tok, M, V, kb[0]);
+  int cur = 0;
+  for (int L = SORT_RUN; L < M; L *= 2, cur ^= 1)
+    k_merge_runs<<<cdiv(M, 256), 256, 0, st>>>(kb[cur], kb[cur ^ 1], M, L);
+  const uint32_t* keys = kb[cur];
   k_emb_seg1<<<nch, 256, 0, st>>>(keys, dh, dwte, M, C, pfirst, plast);
   k_emb_seg2<<<nch, 256, 0, st>>>(keys, dwte, M, C, pfirst, plast);
   k_dwpe<<<dim3(cdiv(C, 256), block_size), 256, 0, st>>>(dh, dwpe, B, T, C, block_size, beta);

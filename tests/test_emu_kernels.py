@@ -137,11 +137,14 @@ def test_emu_tn_gemm_real_weight_shapes(L, M, N):
 
 # ---------------------------------------------------------------------------- embedding backward
 
-@pytest.mark.parametrize("B,T", [(16, 1024), (3, 100)])
+@pytest.mark.parametrize("B,T", [(16, 1024), (3, 100), (1, 1), (1, 1024), (3, 1000), (32, 1024)])
 def test_emu_embedding_backward_zipf(L, B, T):
     """dwte[id] += sum of the residual-gradient rows holding id (deterministic
     sort + segmented sums over the Zipf ids of the benchmark batch);
-    dwpe[t] = beta dwpe[t] + sum_b dh[b, t]."""
+    dwpe[t] = beta dwpe[t] + sum_b dh[b, t].  The (id, position) keys left in
+    the workspace by the sort (runs of 1024, then merge passes) are bitwise
+    those of a plain sort: one position, exactly one run, an odd number of
+    runs, and the 32768-position maximum."""
     C, V, bs = 768, 50257, 1024
     M = B * T
     rng = np.random.default_rng(M)
@@ -152,6 +155,11 @@ def test_emu_embedding_backward_zipf(L, B, T):
     dwte, dwpe = dwte0.copy(), dwpe0.copy()
     ws = np.zeros(L.emu_embed_bwd_ws(M, C) // 4 + 64, np.float32)
     assert L.emu_embed_bwd(ptr(tok), ptr(dh), ptr(dwte), ptr(dwpe), B, T, C, V, bs, 1.0, ptr(ws)) == 0
+    runs = -(-M // 1024)
+    passes = int(np.ceil(np.log2(runs))) if runs > 1 else 0
+    keys = ws.view(np.uint32)[(passes % 2) * runs * 1024:][:M]
+    want = np.sort((tok.astype(np.uint64) << 15 | np.arange(M, dtype=np.uint64)).astype(np.uint32))
+    assert np.array_equal(keys, want)
     ref = dwte0.astype(np.float64)
     np.add.at(ref, tok, dh.astype(np.float64))
     close(dwte, ref, 1e-6, "dwte")
@@ -164,55 +172,73 @@ def test_emu_embedding_backward_zipf(L, B, T):
 
 # ---------------------------------------------------------------------------- cross-entropy
 
-@pytest.mark.parametrize("V,Vp", [(50257, 50304), (50257, 50257)])
-def test_emu_cross_entropy_classifier_rows(L, V, Vp):
+@pytest.mark.parametrize("V,Vp,ld,dt", [(50257, 50304, 50304, 1), (50257, 50257, 50304, 1), (50257, 50304, 50304, 2),
+                                        (301, 320, 320, 0), (1000, 1000, 1024, 2), (37, 37, 64, 1),
+                                        (50257, 50304, 50304, 0)])
+def test_emu_cross_entropy_classifier_rows(L, V, Vp, ld, dt):
     """Per-row loss and the in-place gradient (softmax - onehot) * scale over
-    rows of 50304 (padded) and 50257 logits (row stride 50304), bf16."""
-    M, ld = 64, 50304
-    rng = np.random.default_rng(Vp)
-    z = bf16(rng.standard_normal((M, ld)) * 2.0)
+    rows of Vp logits (stride ld, targets below V): the 124M classifier rows
+    (50304 padded, 50257 unpadded with a one-element last chunk) in bf16,
+    fp16 and fp32 (the streaming kernel), a short fp32 row, and rows shorter
+    than one chunk per thread; targets include the first and the last valid
+    id."""
+    M = 64
+    tt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dt]
+    rng = np.random.default_rng(Vp + dt)
+    z = torch.from_numpy((rng.standard_normal((M, ld)) * 2.0).astype(np.float32)).to(tt)
     tgt = rng.integers(0, V, M).astype(np.int32)
+    tgt[0], tgt[1] = 0, V - 1
     losses = np.zeros(M, np.float32)
     flag = np.zeros(4, np.int32)
     z64 = f64(z)[:, :Vp]
     scale = 1.0 / M
-    assert L.emu_xent(ptr(z), 1, ld, Vp, V, ptr(tgt), ptr(losses), scale, 1, M, ptr(flag)) == 0
+    assert L.emu_xent(ptr(z), dt, ld, Vp, V, ptr(tgt), ptr(losses), scale, 1, M, ptr(flag)) == 0
     lse = np.log(np.exp(z64 - z64.max(1, keepdims=True)).sum(1)) + z64.max(1)
     close(losses, lse - z64[np.arange(M), tgt], 1e-5, "loss")
     g = O.cross_entropy_grad(z64, tgt, 1.0)  # (softmax - onehot) / M
     got = f64(z)
     close(got[:, :Vp], g, 2 ** -7, "dlogits")
+    ty = got[np.arange(M), tgt]
+    close(ty, g[np.arange(M), tgt], 2 ** -7, "dlogits at the targets")
     assert np.all(got[:, Vp:] == 0)
     assert flag[0] == 0
 
 
 # ---------------------------------------------------------------------------- LayerNorm, column sums
 
-def test_emu_layernorm_forward_backward_16384_rows(L):
-    M, C = 16384, 768
-    rng = np.random.default_rng(7)
+@pytest.mark.parametrize("M,C,dt,accum", [(16384, 768, 1, 1), (301, 768, 2, 0), (37, 64, 0, 1), (1, 1024, 1, 0),
+                                          (2053, 256, 1, 1)])
+def test_emu_layernorm_forward_backward_16384_rows(L, M, C, dt, accum):
+    """LayerNorm forward and backward against the oracle: the 124M shape
+    (16384 rows of 768), row counts that leave blocks with ragged and single
+    rows (the backward's next-row prefetch runs out at different points),
+    the widest row (1024), bf16 / fp16 / fp32 activations, with and without
+    accumulation into the residual gradient."""
+    tt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dt]
+    rng = np.random.default_rng(7 + M)
     x = rng.standard_normal((M, C)).astype(np.float32) * 3 + 1
     w = (1 + 0.1 * rng.standard_normal(C)).astype(np.float32)
     b = (0.1 * rng.standard_normal(C)).astype(np.float32)
-    y = torch.zeros((M, C), dtype=torch.bfloat16)
+    y = torch.zeros((M, C), dtype=tt)
     mean = np.zeros(M, np.float32)
     rstd = np.zeros(M, np.float32)
-    assert L.emu_ln_fwd(ptr(x), ptr(w), ptr(b), ptr(y), 1, ptr(mean), ptr(rstd), M, C, 1e-5) == 0
+    assert L.emu_ln_fwd(ptr(x), ptr(w), ptr(b), ptr(y), dt, ptr(mean), ptr(rstd), M, C, 1e-5) == 0
     yr, (xh, rs) = O.layernorm_fwd(x, w, b, 1e-5, np.float64)
     close(f64(y), yr, 2 ** -8, "ln y")
     close(rstd, rs[:, 0], 1e-6, "rstd")
-    dy = bf16(rng.standard_normal((M, C)))
+    dy = torch.from_numpy(rng.standard_normal((M, C)).astype(np.float32)).to(tt)
     dres0 = rng.standard_normal((M, C)).astype(np.float32)
     dres = dres0.copy()
-    dres_act = torch.zeros((M, C), dtype=torch.bfloat16)
+    dres_act = torch.zeros((M, C), dtype=tt)
     part = np.zeros(L.emu_ln_bwd_part_floats(M, C), np.float32)
     dw0 = rng.standard_normal(C).astype(np.float32)
     dw, db = dw0.copy(), np.zeros(C, np.float32)
-    assert L.emu_ln_bwd(ptr(x), ptr(mean), ptr(rstd), ptr(w), ptr(dy), 1, ptr(dres), ptr(dres_act), 1,
+    assert L.emu_ln_bwd(ptr(x), ptr(mean), ptr(rstd), ptr(w), ptr(dy), dt, ptr(dres), ptr(dres_act), accum,
                         ptr(part), M, C, ptr(dw), ptr(db), 1.0) == 0
     dx, dwr, dbr = O.layernorm_bwd(f64(dy), (xh, rs), w, np.float64)
-    close(dres, dres0 + dx, 1e-5, "dx accumulated")
-    close(f64(dres_act), dres0 + dx, 2 ** -8, "bf16 copy")
+    want = dres0 + dx if accum else dx
+    close(dres, want, 1e-5, "dx")
+    close(f64(dres_act), want, 2 ** -8, "16-bit copy")
     close(dw, dw0 + dwr, 1e-5, "dw")
     close(db, dbr, 1e-5, "db")
 
