@@ -16,9 +16,10 @@
 // probabilities feed the next MFMA straight from registers.  exp2 with the
 // scale folded into log2 units.
 //   forward: O and the row log-sum-exp (log2 units) per query.
-//   backward: D = rowsum(dO * O); dQ kernel (query-block parallel) and
-//   dK/dV kernel (key-block parallel), both recomputing P from the saved
-//   log-sum-exp; no atomics, so results are deterministic.
+//   backward: D = rowsum(dO * O) (computed by the dQ kernel); dQ kernel
+//   (query-block parallel) and dK/dV kernel (key-block parallel), both
+//   recomputing P from the saved log-sum-exp; no atomics, so results are
+//   deterministic.
 // Other head sizes / fp32: simple one-thread-per-row kernels.
 #include "common.h"
 #include "kernels.h"
@@ -335,11 +336,14 @@ __device__ __forceinline__ void attn_dq_tile(const uint16_t* Ks, const uint16_t*
   }
 }
 
+// Also computes D = rowsum(dO * O) for its queries (lanes l and l + 32 hold
+// the two halves of a query's 64 dimensions) and writes it for the dK/dV
+// kernel, which runs after it.
 template <typename TE>
-__global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
+__global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv, const TE* __restrict__ o,
                                                    const TE* __restrict__ dout,
                                                    const float* __restrict__ lse,
-                                                   const float* __restrict__ Dv,
+                                                   float* __restrict__ Dv,
                                                    TE* __restrict__ dqkv, int T, int H, float sl2,
                                                    float scale) {
   typedef typename H16<TE>::v8 v8;
@@ -357,15 +361,19 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv,
   const TE* vp = base + 2 * C + h * 64;
 
   v8 qf[4], dof[4];
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     qf[ks] = __builtin_bit_cast(
         v8, q < T ? ldg16(base + (size_t)q * ld + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
-    dof[ks] = __builtin_bit_cast(
-        v8, q < T ? ldg16(dob + (size_t)q * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0));
+    const uint4 du = q < T ? ldg16(dob + (size_t)q * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0);
+    const uint4 ou = q < T ? ldg16(o + ((size_t)b * T + q) * C + h * 64 + ks * 16 + g * 8) : make_uint4(0, 0, 0, 0);
+    dof[ks] = __builtin_bit_cast(v8, du);
+    dpart += dot16<TE>(du, ou);
   }
   const float lq = q < T ? lse[(size_t)bh * T + q] : 0.f;
-  const float Dq = q < T ? Dv[(size_t)bh * T + q] : 0.f;
+  const float Dq = dpart + __shfl_xor(dpart, 32, 64);
+  if (g == 0 && q < T) Dv[(size_t)bh * T + q] = Dq;
   f32x16 dq[2] = {zero16(), zero16()};
   const int qlast = min(q0 + 127, T - 1);
   const int ntiles = qlast / 64 + 1;
@@ -678,17 +686,17 @@ template <typename TA>
 static hipError_t attn_bwd_t(const void* qkv, const void* o, const void* dout, const float* lse, void* dqkv,
                              float* ws, int B, int T, int H, int hd, float sl2, float scale, hipStream_t st) {
   const int n = B * T * H;
-  k_attn_bwd_pre<TA><<<cdiv(n, 256), 256, 0, st>>>((const TA*)o, (const TA*)dout, ws, B, T, H, hd);
   if constexpr (sizeof(TA) == 2) {
-    if (hd == 64) {
+    if (hd == 64) {  // the dQ kernel computes D itself
       dim3 grid(cdiv(T, 128), B * H);
-      k_attn_dq64<TA><<<grid, 256, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, T, H, sl2,
-                                            scale);
+      k_attn_dq64<TA><<<grid, 256, 0, st>>>((const TA*)qkv, (const TA*)o, (const TA*)dout, lse, ws, (TA*)dqkv, T,
+                                            H, sl2, scale);
       k_attn_dkv64<TA><<<grid, 256, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, T, H, sl2,
                                              scale);
       return hipGetLastError();
     }
   }
+  k_attn_bwd_pre<TA><<<cdiv(n, 256), 256, 0, st>>>((const TA*)o, (const TA*)dout, ws, B, T, H, hd);
   const int g = cdiv((long)B * H * T, 128);
   k_attn_dq_gen<TA, 128><<<g, 128, 0, st>>>((const TA*)qkv, (const TA*)dout, lse, ws, (TA*)dqkv, B, T, H, hd,
                                             sl2, scale);

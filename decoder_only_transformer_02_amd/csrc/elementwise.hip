@@ -329,8 +329,17 @@ __global__ __launch_bounds__(256) void k_ln_param_reduce1(const float* __restric
   int per = (nblk + LNR_SLICES - 1) / LNR_SLICES;
   int r0 = blockIdx.z * per, r1 = min(r0 + per, nblk);
   float s = 0.f;
-  if (c < C)
-    for (int r = r0 + grp; r < r1; r += 4) s += part[((size_t)r * 2 + wb) * C + c];
+  if (c < C) {  // rows r0 + grp, + 4, ... in order; four loads in flight at a time
+    int r = r0 + grp;
+    for (; r + 12 < r1; r += 16) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[((size_t)(r + 4 * u) * 2 + wb) * C + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; r < r1; r += 4) s += part[((size_t)r * 2 + wb) * C + c];
+  }
   red[grp][threadIdx.x & 63] = s;
   __syncthreads();
   if (grp == 0 && c < C) {
@@ -361,13 +370,24 @@ hipError_t ln_param_grad_reduce(const float* part, int nblk, float* dw, float* d
 int ln_bwd_part_floats(int M, int C) { return (ln_bwd_blocks(M) + LNR_SLICES) * 2 * C; }
 
 // ------------------------------------------------------------------ bias-gradient column sums
-int colsum_parts(int M) {
-  int r = cdiv(M, 256);
-  return r < 64 ? r : 64;
+// db[n] = beta db[n] + sum_m X[m][n] in two deterministic stages.  Stage 1
+// splits the rows into R slices so that the grid has about 1024 blocks
+// whatever N is (a block covers 256 columns of one slice: 32 threads x 8
+// columns, 16-byte loads, 8 row groups); stage 2 has 16 row groups per 16
+// columns walk the R partial rows, four loads in flight each, and combines
+// the groups in a fixed order.  R * N <= 1024 * 256 floats.
+constexpr int COLSUM_BLOCKS = 1024;
+
+static int colsum_slices(int M, int N) {
+  const int nb = cdiv(N, 256);
+  int r = COLSUM_BLOCKS / nb;
+  r = r < 1 ? 1 : r;
+  const int rmax = cdiv(M, 16);  // at least 16 rows per slice
+  return r < rmax ? r : rmax;
 }
 
-// Stage 1: a block covers 256 columns (32 threads x 8 columns, 16-byte
-// loads) and 8 row groups over one slice of rows; stage 2 sums the slices.
+size_t colsum_part_floats(int M, int N) { return (size_t)colsum_slices(M, N) * N; }
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum_part(const T* __restrict__ X, int M, int N, int ldx,
                                                      int rows_per, float* __restrict__ part) {
@@ -408,18 +428,37 @@ __global__ __launch_bounds__(256) void k_colsum_part(const T* __restrict__ X, in
 
 __global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ part, int R, int N,
                                                       float* db, float beta) {
-  int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[16][16];
+  const int c = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int n = blockIdx.x * 16 + c;
   float s = 0.f;
-  for (int r = 0; r < R; ++r) s += part[(size_t)r * N + n];
-  db[n] = (beta != 0.f ? beta * db[n] : 0.f) + s;
+  if (n < N) {  // rows grp, grp + 16, ... in order
+    int r = grp;
+    for (; r + 48 < R; r += 64) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[(size_t)(r + 16 * u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; r < R; r += 16) s += part[(size_t)r * N + n];
+  }
+  red[grp][c] = s;
+  __syncthreads();
+  if (grp == 0 && n < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][c];
+    db[n] = (beta != 0.f ? beta * db[n] : 0.f) + t;
+  }
 }
 
 hipError_t colsum(const void* X, int dt, int M, int N, int ldx, float* db, float beta,
                   float* part, hipStream_t st) {
-  if (N % 8 || ldx % 8) return hipErrorInvalidValue;
-  int R = colsum_parts(M);
+  if (N % 8 || ldx % 8 || M < 1) return hipErrorInvalidValue;
+  int R = colsum_slices(M, N);
   int rows_per = cdiv(M, R);
+  R = cdiv(M, rows_per);  // slices that hold rows
   dim3 g(cdiv(N, 256), R);
   if (dt == ACT_BF16)
     k_colsum_part<bf16><<<g, 256, 0, st>>>((const bf16*)X, M, N, ldx, rows_per, part);
@@ -427,7 +466,7 @@ hipError_t colsum(const void* X, int dt, int M, int N, int ldx, float* db, float
     k_colsum_part<f16><<<g, 256, 0, st>>>((const f16*)X, M, N, ldx, rows_per, part);
   else
     k_colsum_part<float><<<g, 256, 0, st>>>((const float*)X, M, N, ldx, rows_per, part);
-  k_colsum_final<<<cdiv(N, 256), 256, 0, st>>>(part, R, N, db, beta);
+  k_colsum_final<<<cdiv(N, 16), 256, 0, st>>>(part, R, N, db, beta);
   return hipGetLastError();
 }
 
@@ -888,7 +927,17 @@ __global__ __launch_bounds__(256) void k_sumsq(const float* __restrict__ g, size
   size_t n4 = n / 4;
   float s = 0.f;
   const float4* g4 = (const float4*)g;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  // four grid-strided loads in flight at a time, summed in the same order
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = g4[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += (v[u].x * v[u].x + v[u].y * v[u].y) + (v[u].z * v[u].z + v[u].w * v[u].w);
+  }
+  for (; i < n4; i += stride) {
     float4 v = g4[i];
     s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
   }
@@ -988,23 +1037,39 @@ __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const floa
   float wdl = (ck.flags & 1) ? wd : 0.f;
   bool wsh = (ck.flags & 2) != 0;
   size_t end = ck.start + ck.count;
-  for (size_t i = ck.start + (size_t)threadIdx.x * 4; i < end; i += 256 * 4) {
-    float4 pp = *(float4*)(p + i), gg = *(const float4*)(g + i);
-    float4 mm = *(float4*)(m + i), vv = *(float4*)(v + i);
-    float pa[4] = {pp.x, pp.y, pp.z, pp.w}, ga[4] = {gg.x, gg.y, gg.z, gg.w};
-    float ma[4] = {mm.x, mm.y, mm.z, mm.w}, va[4] = {vv.x, vv.y, vv.z, vv.w};
+  // two groups of 4 elements per thread and iteration (the second 1024
+  // elements further on), all eight loads issued before any update
+  for (size_t i0 = ck.start + (size_t)threadIdx.x * 4; i0 < end; i0 += 2 * 256 * 4) {
+    const bool two = i0 + 256 * 4 < end;
+    float4 pp[2], gg[2], mm[2], vv[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float gj = ga[j] * coef;
-      ma[j] = beta1 * ma[j] + (1.0f - beta1) * gj;
-      va[j] = beta2 * va[j] + (1.0f - beta2) * gj * gj;
-      float mh = ma[j] * inv_bc1, vh = va[j] * inv_bc2;
-      pa[j] = pa[j] - lr * (mh / (sqrtf(vh) + eps) + wdl * pa[j]);
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      const size_t i = i0 + (size_t)h * 256 * 4;
+      pp[h] = *(float4*)(p + i);
+      gg[h] = *(const float4*)(g + i);
+      mm[h] = *(float4*)(m + i);
+      vv[h] = *(float4*)(v + i);
     }
-    *(float4*)(p + i) = make_float4(pa[0], pa[1], pa[2], pa[3]);
-    *(float4*)(m + i) = make_float4(ma[0], ma[1], ma[2], ma[3]);
-    *(float4*)(v + i) = make_float4(va[0], va[1], va[2], va[3]);
-    if (wsh) *(uint2*)(shadow + i) = make_uint2(H16<TS>::pack2(pa[0], pa[1]), H16<TS>::pack2(pa[2], pa[3]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      const size_t i = i0 + (size_t)h * 256 * 4;
+      float pa[4] = {pp[h].x, pp[h].y, pp[h].z, pp[h].w}, ga[4] = {gg[h].x, gg[h].y, gg[h].z, gg[h].w};
+      float ma[4] = {mm[h].x, mm[h].y, mm[h].z, mm[h].w}, va[4] = {vv[h].x, vv[h].y, vv[h].z, vv[h].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float gj = ga[j] * coef;
+        ma[j] = beta1 * ma[j] + (1.0f - beta1) * gj;
+        va[j] = beta2 * va[j] + (1.0f - beta2) * gj * gj;
+        float mh = ma[j] * inv_bc1, vh = va[j] * inv_bc2;
+        pa[j] = pa[j] - lr * (mh / (sqrtf(vh) + eps) + wdl * pa[j]);
+      }
+      *(float4*)(p + i) = make_float4(pa[0], pa[1], pa[2], pa[3]);
+      *(float4*)(m + i) = make_float4(ma[0], ma[1], ma[2], ma[3]);
+      *(float4*)(v + i) = make_float4(va[0], va[1], va[2], va[3]);
+      if (wsh) *(uint2*)(shadow + i) = make_uint2(H16<TS>::pack2(pa[0], pa[1]), H16<TS>::pack2(pa[2], pa[3]));
+    }
   }
 }
 

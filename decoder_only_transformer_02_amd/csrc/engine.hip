@@ -4,6 +4,7 @@
 // kernels live in elementwise.hip, gemm.hip and attention.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -336,7 +337,9 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t o_dqkv = pl.add("d_qkv", GPT2_K_ACT, adt, {maxM, 3 * C});
   size_t o_du = pl.add("d_fc_u", GPT2_K_ACT, adt, {maxM, 4 * C});
   size_t o_lnp = pl.raw((size_t)gk::ln_bwd_part_floats((int)maxM, C) * 4, "LayerNorm partials");
-  size_t o_colp = pl.raw((size_t)gk::colsum_parts((int)maxM) * 4 * C * 4, "column-sum partials");
+  size_t ncolp = 0;  // bias-gradient column sums run over N = C, 3C, 4C
+  for (int n : {C, 3 * C, 4 * C}) ncolp = std::max(ncolp, gk::colsum_part_floats((int)maxM, n));
+  size_t o_colp = pl.raw(ncolp * 4, "column-sum partials");
   size_t sk = 0;
   {
     const int64_t shapes[5][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}, {c.padded_vocab, C}};
@@ -839,7 +842,7 @@ gpt2_status start_forward(gpt2_ctx* c, const int32_t* d_tokens, int32_t B, int32
   c->armed_bwd = false;
   c->B = B;
   c->T = T;
-  HIPCHK(c, hipMemsetAsync(c->flag, 0, 16, c->st));
+  HIPCHK(c, gk::fill_f32((float*)c->flag, 4, 0.f, c->st));  // a kernel, not a memset node, should a caller capture this
   HIPCHK(c, hipMemcpyAsync(c->tok, d_tokens, (size_t)B * T * 4, hipMemcpyDeviceToDevice, c->st));
   return GPT2_OK;
 }
@@ -885,7 +888,7 @@ GPT2_API gpt2_status gpt2_generate(gpt2_ctx* c, void* d_kv_cache, size_t kv_byte
   const size_t layer_bytes = (size_t)c->cfg.max_batch * c->cfg.max_seq * 2 * C * c->act_es;
   auto cache = [&](int l) { return (void*)((char*)d_kv_cache + (size_t)l * layer_bytes); };
   c->armed_bwd = false;
-  HIPCHK(c, hipMemsetAsync(c->flag, 0, 16, c->st));
+  HIPCHK(c, gk::fill_f32((float*)c->flag, 4, 0.f, c->st));  // a kernel, not a memset node, should a caller capture this
   // prefill: the prefix through the ordinary forward, its keys and values
   // into the cache, then the first new token from the last prefix position
   HIPCHK(c, hipMemcpy2DAsync(c->tok, (size_t)T0 * 4, d_tokens, (size_t)T_total * 4, (size_t)T0 * 4, B,

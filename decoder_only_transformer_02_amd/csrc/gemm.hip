@@ -952,8 +952,20 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
                                                        float beta) {
   const size_t n4 = n / 4;  // n is a multiple of 4 (N % 4 == 0 when split)
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    // the partials are added in split order; loads go out 8 at a time so
+    // their latencies overlap instead of adding up
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int z = 0; z < S; ++z) {
+    int z = 0;
+    for (; z + 8 <= S; z += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *(const float4*)(ws + (size_t)(z + u) * n + 4 * i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+    for (; z < S; ++z) {
       float4 v = *(const float4*)(ws + (size_t)z * n + 4 * i);
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }

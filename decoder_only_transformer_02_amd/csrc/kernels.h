@@ -30,7 +30,7 @@ hipError_t ln_param_grad_reduce(const float* part, int nblk, float* dw, float* d
                                 float beta, hipStream_t st);
 // Column sums of an activation matrix X[M, N] (row stride ldx): db = beta *
 // db + sum_m X[m, :], deterministic two-stage reduction through `part`.
-int colsum_parts(int M);
+size_t colsum_part_floats(int M, int N);  // partials buffer of colsum for an M x N input
 hipError_t colsum(const void* X, int dt, int M, int N, int ldx, float* db, float beta,
                   float* part, hipStream_t st);
 // Fused softmax cross-entropy over the first V columns: per-row loss into

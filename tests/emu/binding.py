@@ -40,7 +40,7 @@ def emu_lib():
             "emu_ln_fwd": (I, [P, P, P, P, I, P, P, I, I, F]),
             "emu_ln_bwd_part_floats": (I, [I, I]),
             "emu_ln_bwd": (I, [P, P, P, P, P, I, P, P, I, P, I, I, P, P, F]),
-            "emu_colsum_parts": (I, [I]),
+            "emu_colsum_part_floats": (SZ, [I, I]),
             "emu_colsum": (I, [P, I, I, I, I, P, F, P]),
             "emu_transpose_jobs": (I, [P, P, P, I, I]),
         }

@@ -61,7 +61,7 @@ EMU_API int emu_ln_bwd(const float* x, const float* mean, const float* rstd, con
   return (int)gk::ln_param_grad_reduce(part, gk::ln_bwd_blocks(M), dw, db, C, beta, nullptr);
 }
 
-EMU_API int emu_colsum_parts(int M) { return gk::colsum_parts(M); }
+EMU_API size_t emu_colsum_part_floats(int M, int N) { return gk::colsum_part_floats(M, N); }
 
 EMU_API int emu_colsum(const void* X, int dt, int M, int N, int ldx, float* db, float beta, float* part) {
   return (int)gk::colsum(X, dt, M, N, ldx, db, beta, part, nullptr);

@@ -243,15 +243,24 @@ def test_emu_layernorm_forward_backward_16384_rows(L, M, C, dt, accum):
     close(db, dbr, 1e-5, "db")
 
 
-def test_emu_bias_column_sums(L):
-    M, N = 16384, 3072
-    rng = np.random.default_rng(3)
-    X = bf16(rng.standard_normal((M, N)))
+@pytest.mark.parametrize("M,N,dt", [(16384, 3072, 1), (16384, 768, 1), (16384, 2304, 2), (300, 768, 1), (7, 64, 0),
+                                    (1, 8, 1)])
+def test_emu_bias_column_sums(L, M, N, dt):
+    """Bias gradients as two-stage column sums: the 124M shapes (16384 rows
+    of 3072, 768 and 2304 columns), a ragged row count, a handful of rows
+    (fewer than one 16-row slice) and a single row; accumulating into db."""
+    tt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dt]
+    rng = np.random.default_rng(M + N)
+    X = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(tt)
     db0 = rng.standard_normal(N).astype(np.float32)
     db = db0.copy()
-    part = np.zeros(L.emu_colsum_parts(M) * N, np.float32)
-    assert L.emu_colsum(ptr(X), 1, M, N, N, ptr(db), 1.0, ptr(part)) == 0
+    part = np.zeros(L.emu_colsum_part_floats(M, N), np.float32)
+    assert part.size <= 1024 * 256
+    assert L.emu_colsum(ptr(X), dt, M, N, N, ptr(db), 1.0, ptr(part)) == 0
     close(db, db0 + f64(X).sum(0), 1e-5, "column sums")
+    db2 = db0.copy()
+    assert L.emu_colsum(ptr(X), dt, M, N, N, ptr(db2), 0.0, ptr(part)) == 0
+    close(db2, f64(X).sum(0), 1e-5, "column sums, beta 0")
 
 
 def test_emu_transpose_jobs_ragged(L):
@@ -315,6 +324,7 @@ def test_emu_flash_attention_forward_backward(L, B, T, H, dt):
     ws = np.zeros(L.emu_attn_bwd_ws(B, T, H), np.float32)
     assert L.emu_attn_bwd(ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws), B, T, H, hd, dt) == 0
     do = f64(dout).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    close(ws.reshape(B, H, T), (do * og).sum(-1), 1e-5, "D = rowsum(dO * O), left in the workspace")
     dq, dk, dv = O.causal_attention_bwd(q, k, v, og, do, np.float64)
     got = f64(dqkv).reshape(B, T, 3, H, hd).transpose(2, 0, 3, 1, 4)
     for i, (name, r) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
