@@ -515,6 +515,32 @@ __device__ __forceinline__ float chunk_elem<f16>(const uint4& u, int j) {
   return (j & 1) ? H16<f16>::hi(w) : H16<f16>::lo(w);
 }
 
+// Element j of a chunk through shift and mask amounts the compiler cannot
+// see as constants (read from LDS after a barrier).  The cross-entropy
+// converts its register-held row afresh in each pass this way: otherwise
+// the compiler keeps all 200 converted values of the first pass live for
+// the later ones, which takes the kernel to 256 registers and one wave
+// per SIMD.  `sh` is 16 and `mask` 0xffff0000.
+struct Opaque {
+  uint32_t sh, mask;
+};
+template <typename T>
+__device__ __forceinline__ float chunk_elem_o(const uint4& u, int j, Opaque o);
+template <>
+__device__ __forceinline__ float chunk_elem_o<float>(const uint4& u, int j, Opaque) {
+  return chunk_elem<float>(u, j);
+}
+template <>
+__device__ __forceinline__ float chunk_elem_o<bf16>(const uint4& u, int j, Opaque o) {
+  uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
+  return __uint_as_float((j & 1) ? (w & o.mask) : (w << o.sh));
+}
+template <>
+__device__ __forceinline__ float chunk_elem_o<f16>(const uint4& u, int j, Opaque o) {
+  uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
+  return (j & 1) ? H16<f16>::lo(w >> o.sh) : H16<f16>::lo(w & ~o.mask);
+}
+
 template <typename T>
 __device__ __forceinline__ uint4 chunk_pack(const float* f);
 template <>
@@ -576,11 +602,11 @@ __device__ __forceinline__ uint4 chunk_keep(uint4 u, int n) {
 //
 // The element loops carry no per-element tests: the one chunk that
 // straddles V is padded with -inf at its load and chunks past V are all
-// -inf, so the max, the sum and the gradient need no bounds checks; the
-// target logit is read from the registers of the thread that holds it, and
-// the "- 1" of the target's gradient is written by that thread as one
-// element after its chunk store (same thread, same address: the later
-// store wins).
+// -inf, so the max, the sum and the gradient need no bounds checks.  The
+// thread that owns the target's chunk reads the target logit itself before
+// the first barrier (nobody else writes that chunk, and it writes it only
+// after the reductions), skips that chunk in the gradient loop, and then
+// reloads it and writes its gradient with the "- 1" applied.
 template <typename T, int NCH, bool DS>
 __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, int V, int vt,
                                               const int32_t* __restrict__ tgt,
@@ -589,6 +615,7 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
   constexpr int E = Chunk16<T>::E;
   __shared__ float sh[4];
   __shared__ float sh_zy;
+  __shared__ Opaque sh_opq;
   int row = blockIdx.x;
   T* z = logits + (size_t)row * ld;
   int y = tgt[row];
@@ -596,17 +623,20 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
     if (threadIdx.x == 0) atomicOr(flag, FLAG_TARGET);
     y = y < 0 ? 0 : vt - 1;
   }
+  if (threadIdx.x == 0) sh_opq = Opaque{16u, 0xffff0000u};
   const int ych = y / E;
+  const int kown = ych / 256, town = ych % 256, yo = y - ych * E;  // the target's chunk: pass, thread, slot
+  if ((int)threadIdx.x == town) sh_zy = to_f(z[y]);
   uint4 buf[NCH];
+  // The tests on k alone are uniform (scalar branches): only the last
+  // passes, whose chunks can reach ld or V, pay for the per-thread tests.
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int e0 = (threadIdx.x + k * 256) * E;
-    buf[k] = e0 < ld ? *(const uint4*)(z + e0) : chunk_neginf<T>();
-    if (e0 + E > V) buf[k] = chunk_keep<T>(buf[k], V - e0);  // n <= 0: all -inf
+    if ((k + 1) * 256 * E <= ld) buf[k] = *(const uint4*)(z + e0);
+    else buf[k] = e0 < ld ? *(const uint4*)(z + e0) : chunk_neginf<T>();
+    if ((k + 1) * 256 * E > V && e0 + E > V) buf[k] = chunk_keep<T>(buf[k], V - e0);  // n <= 0: all -inf
   }
-#pragma unroll
-  for (int k = 0; k < NCH; ++k)
-    if ((int)threadIdx.x + k * 256 == ych) sh_zy = chunk_elem<T>(buf[k], y - ych * E);
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NCH; ++k)
@@ -616,28 +646,41 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
   const float zy = sh_zy;
   const float mx2 = mx * LOG2E;
   float s = 0.f;
+  const Opaque o2 = sh_opq;  // read after the reduction's barriers
 #pragma unroll
   for (int k = 0; k < NCH; ++k)
 #pragma unroll
-    for (int j = 0; j < E; ++j) s += __builtin_amdgcn_exp2f(fmaf(chunk_elem<T>(buf[k], j), LOG2E, -mx2));
+    for (int j = 0; j < E; ++j) s += __builtin_amdgcn_exp2f(fmaf(chunk_elem_o<T>(buf[k], j, o2), LOG2E, -mx2));
   s = block_reduce_sum(s, sh);
   float lse = mx + __logf(s);
   if (threadIdx.x == 0) losses[row] = lse - zy;
   if (!want_grad) return;
   if constexpr (DS) scale *= dev_scale[0];
   const float lse2 = lse * LOG2E;
+  const Opaque o3 = sh_opq;  // read after the second reduction's barriers
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int e0 = (threadIdx.x + k * 256) * E;
-    if (e0 < ld) {
+    if ((k + 1) * 256 * E <= ld || e0 < ld) {
       float f[E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) f[j] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<T>(buf[k], j), LOG2E, -lse2)) * scale;
-      *(uint4*)(z + e0) = chunk_pack<T>(f);
+      for (int j = 0; j < E; ++j)
+        f[j] = __builtin_amdgcn_exp2f(fmaf(chunk_elem_o<T>(buf[k], j, o3), LOG2E, -lse2)) * scale;
+      if (!(k == kown && (int)threadIdx.x == town)) *(uint4*)(z + e0) = chunk_pack<T>(f);
     }
   }
-  if ((int)threadIdx.x == ych % 256)
-    z[y] = from_f<T>((__builtin_amdgcn_exp2f(fmaf(zy, LOG2E, -lse2)) - 1.0f) * scale);
+  if ((int)threadIdx.x == town) {  // the target's chunk, untouched so far
+    const int e0 = ych * E;
+    uint4 u = *(const uint4*)(z + e0);
+    if (e0 + E > V) u = chunk_keep<T>(u, V - e0);
+    float f[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float v = chunk_elem<T>(u, j);
+      f[j] = (__builtin_amdgcn_exp2f(fmaf(v, LOG2E, -lse2)) - (j == yo ? 1.0f : 0.0f)) * scale;
+    }
+    *(uint4*)(z + e0) = chunk_pack<T>(f);
+  }
 }
 
 // Streaming variant (row too long for registers): three passes over HBM.
