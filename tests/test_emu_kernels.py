@@ -378,3 +378,81 @@ def test_emu_fp32_mfma_gemm(L, M, N, K, at, bt, epi):
         close(out, acc * O.gelu_tanh_grad(aux.astype(np.float64)), 1e-5, "gelu derivative")
     else:
         close(out, alpha * acc + beta * out0, 1e-5, "weight gradient")
+
+
+# ---------------------------------------------------------------------------- schedule independence
+
+def _kernel_outputs(L):
+    """Outputs of the LDS-staged and multi-pass kernels on one fixed input
+    each: attention forward and backward over 5 key tiles (both LDS buffers
+    reused), cross-entropy rows, LayerNorm forward and backward, column sums
+    and the embedding-backward sort."""
+    rng = np.random.default_rng(11)
+    out = []
+    B, T, H, hd = 1, 300, 2, 64
+    C = H * hd
+    qkv = bf16(rng.standard_normal((B * T, 3 * C)))
+    o = torch.zeros((B * T, C), dtype=torch.bfloat16)
+    lse = np.zeros(B * H * T, np.float32)
+    assert L.emu_attn_fwd(ptr(qkv), ptr(o), ptr(lse), B, T, H, hd, 1) == 0
+    dout = bf16(rng.standard_normal((B * T, C)))
+    dqkv = torch.zeros((B * T, 3 * C), dtype=torch.bfloat16)
+    ws = np.zeros(L.emu_attn_bwd_ws(B, T, H), np.float32)
+    assert L.emu_attn_bwd(ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws), B, T, H, hd, 1) == 0
+    out += [o.view(torch.int16).numpy().copy(), lse.copy(), dqkv.view(torch.int16).numpy().copy()]
+    M, ld, V = 8, 2048, 2001
+    z = bf16(rng.standard_normal((M, ld)) * 2.0)
+    tgt = rng.integers(0, V, M).astype(np.int32)
+    losses = np.zeros(M, np.float32)
+    flag = np.zeros(4, np.int32)
+    assert L.emu_xent(ptr(z), 1, ld, V, V, ptr(tgt), ptr(losses), 1.0 / M, 1, M, ptr(flag)) == 0
+    out += [z.view(torch.int16).numpy().copy(), losses.copy()]
+    M, C = 700, 768
+    x = rng.standard_normal((M, C)).astype(np.float32)
+    w = rng.standard_normal(C).astype(np.float32)
+    b = rng.standard_normal(C).astype(np.float32)
+    y = torch.zeros((M, C), dtype=torch.bfloat16)
+    mean, rstd = np.zeros(M, np.float32), np.zeros(M, np.float32)
+    assert L.emu_ln_fwd(ptr(x), ptr(w), ptr(b), ptr(y), 1, ptr(mean), ptr(rstd), M, C, 1e-5) == 0
+    dy = bf16(rng.standard_normal((M, C)))
+    dres = np.ones((M, C), np.float32)
+    dres_act = torch.zeros((M, C), dtype=torch.bfloat16)
+    part = np.zeros(L.emu_ln_bwd_part_floats(M, C), np.float32)
+    dw, db = np.zeros(C, np.float32), np.zeros(C, np.float32)
+    assert L.emu_ln_bwd(ptr(x), ptr(mean), ptr(rstd), ptr(w), ptr(dy), 1, ptr(dres), ptr(dres_act), 1,
+                        ptr(part), M, C, ptr(dw), ptr(db), 0.0) == 0
+    out += [y.view(torch.int16).numpy().copy(), dres.copy(), dw.copy(), db.copy()]
+    X = bf16(rng.standard_normal((M, 3 * C)))
+    cs = np.zeros(3 * C, np.float32)
+    cpart = np.zeros(L.emu_colsum_part_floats(M, 3 * C), np.float32)
+    assert L.emu_colsum(ptr(X), 1, M, 3 * C, 3 * C, ptr(cs), 0.0, ptr(cpart)) == 0
+    out.append(cs.copy())
+    Bt, Tt, Ce = 3, 1000, 64
+    tok = inputs.zipf_stream(1, Bt * Tt).astype(np.int32)
+    dh = rng.standard_normal((Bt * Tt, Ce)).astype(np.float32)
+    dwte, dwpe = np.zeros((50304, Ce), np.float32), np.zeros((1024, Ce), np.float32)
+    wse = np.zeros(L.emu_embed_bwd_ws(Bt * Tt, Ce) // 4 + 64, np.float32)
+    assert L.emu_embed_bwd(ptr(tok), ptr(dh), ptr(dwte), ptr(dwpe), Bt, Tt, Ce, 50257, 1024, 0.0, ptr(wse)) == 0
+    out += [dwte.copy(), dwpe.copy()]
+    return out
+
+
+def test_emu_kernels_independent_of_schedule(L):
+    """Bitwise the same outputs with every block's fibers scheduled in
+    reverse order and with buffer-to-LDS writes landing early: a missing
+    barrier between a double-buffered tile's store and another wave's reads,
+    or a pass that reads a value before the reduction that produces it,
+    would show as a difference."""
+    base = _kernel_outputs(L)
+    try:
+        L.emu_set_reverse_order(1)
+        rev = _kernel_outputs(L)
+        L.emu_set_reverse_order(0)
+        L.emu_set_land_early(1)
+        early = _kernel_outputs(L)
+    finally:
+        L.emu_set_reverse_order(0)
+        L.emu_set_land_early(0)
+    for other in (rev, early):
+        for i, (a, b) in enumerate(zip(base, other)):
+            assert np.array_equal(a, b), i
