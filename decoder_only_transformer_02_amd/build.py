@@ -2,12 +2,16 @@
 
 Each source is compiled separately (in parallel) into _build/, then linked
 into decoder_only_transformer_02_amd/libgpt2mi.so.  Packed-fp32 VALU
-instructions are disabled for all device code.
+instructions are disabled for all device code.  The compiler's per-kernel
+resource report (registers, scratch, LDS, occupancy) is kept in
+_build/kernel_resources.json, which a CPU test checks.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
+import re
 import shutil
 import subprocess
 
@@ -32,6 +36,25 @@ def flags():
             "-Wno-unused-command-line-argument"]
 
 
+_FIELDS = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+           "LDS Size [bytes/block]": "lds", "Occupancy [waves/SIMD]": "occupancy"}
+
+
+def parse_resources(stderr: str) -> dict:
+    """Kernel (mangled name) -> {vgpr, agpr, scratch, lds, occupancy} from
+    the -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*): (\d+)", line)
+        if m and cur is not None and m.group(1).strip() in _FIELDS:
+            cur[_FIELDS[m.group(1).strip()]] = int(m.group(2))
+    return {k: v for k, v in out.items() if v}
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     bdir = os.path.join(ROOT, "_build")
@@ -39,16 +62,24 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *flags(), "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-        if verbose and r.stderr.strip():
-            print(r.stderr)
-        return obj
+        if verbose:
+            rest = [ln for ln in r.stderr.splitlines() if "remark" not in ln]
+            if any(ln.strip() for ln in rest):
+                print("\n".join(rest))
+        return obj, parse_resources(r.stderr)
 
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        done = list(ex.map(compile_one, SOURCES))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, d in done:
+        res.update(d)
+    with open(os.path.join(bdir, "kernel_resources.json"), "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
     tmp = OUT + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs, "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
