@@ -880,17 +880,25 @@ __global__ __launch_bounds__(256) void k_emb_seg1(const uint32_t* __restrict__ k
   __syncthreads();
   int prev_id = i0 > 0 ? key_id(keys[i0 - 1]) : -1;
   int next_id = i1 < M ? key_id(keys[i1]) : -1;
+  const int n = i1 - i0;
   for (int c = threadIdx.x; c < C; c += 256) {
+    // the chunk's SEG rows are loaded before any is summed, so their
+    // latencies overlap; the sums below keep the sorted order
+    float v[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) v[i] = i < n ? dh[(size_t)key_pos(ks[i]) * C + c] : 0.f;
     float acc = 0.f;
-    int run_start = i0;
-    for (int i = i0; i < i1; ++i) {
-      uint32_t k = ks[i - i0];
-      acc += dh[(size_t)key_pos(k) * C + c];
-      int id = key_id(k);
-      bool end = (i == i1 - 1) || key_id(ks[i + 1 - i0]) != id;
+    bool at_start = true;  // the current run began at this chunk's first entry
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i >= n) break;
+      acc += v[i];
+      const int id = key_id(ks[i]);
+      const bool last = i == n - 1;
+      const bool end = last || key_id(ks[i + 1]) != id;
       if (end) {
-        bool from_prev = (run_start == i0) && prev_id == id;
-        bool to_next = (i == i1 - 1) && next_id == id;
+        const bool from_prev = at_start && prev_id == id;
+        const bool to_next = last && next_id == id;
         if (!from_prev && !to_next) {
           dwte[(size_t)id * C + c] += acc;
         } else if (from_prev) {
@@ -899,7 +907,7 @@ __global__ __launch_bounds__(256) void k_emb_seg1(const uint32_t* __restrict__ k
           plast[(size_t)ch * C + c] = acc;   // starts a run that continues
         }
         acc = 0.f;
-        run_start = i + 1;
+        at_start = false;
       }
     }
   }
@@ -916,13 +924,36 @@ __global__ __launch_bounds__(256) void k_emb_seg2(const uint32_t* __restrict__ k
   int id = key_id(keys[i1 - 1]);
   if (i1 >= M || key_id(keys[i1]) != id) return;                       // does not continue
   if (i0 > 0 && key_id(keys[i0]) == id && key_id(keys[i0 - 1]) == id) return;  // not its start
+  // The run's last chunk kend first: the block tests 256 chunk borders at a
+  // time and keeps the smallest chunk where the run stops (the early returns
+  // above depend on the chunk alone, so every thread reaches the barriers).
+  // Then the sum over chunks ch + 1 .. kend, in order, four loads in flight.
+  __shared__ int s_end;
+  if (threadIdx.x == 0) s_end = nch;
+  __syncthreads();
+  for (int base = ch + 1; base < nch; base += 256) {
+    const int k = base + (int)threadIdx.x;
+    if (k < nch) {
+      const int e = min((k + 1) * SEG, M);
+      if (e >= M || key_id(keys[e]) != id || key_id(keys[e - 1]) != id) atomicMin(&s_end, k);
+    }
+    __syncthreads();
+    const int found = s_end;
+    __syncthreads();  // every thread has read s_end before the next round's updates
+    if (found < nch) break;
+  }
+  const int kend = s_end;
   for (int c = threadIdx.x; c < C; c += 256) {
     float acc = plast[(size_t)ch * C + c];
-    for (int k = ch + 1; k < nch; ++k) {
-      acc += pfirst[(size_t)k * C + c];
-      int e = min((k + 1) * SEG, M);
-      if (e >= M || key_id(keys[e]) != id || key_id(keys[e - 1]) != id) break;
+    int k = ch + 1;
+    for (; k + 3 <= kend; k += 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = pfirst[(size_t)(k + u) * C + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += v[u];
     }
+    for (; k <= kend; ++k) acc += pfirst[(size_t)k * C + c];
     dwte[(size_t)id * C + c] += acc;
   }
 }
@@ -934,8 +965,17 @@ __global__ __launch_bounds__(256) void k_dwpe(const float* __restrict__ dh, floa
   int t = blockIdx.y;
   if (c >= C) return;
   float s = 0.f;
-  if (t < T)
-    for (int b = 0; b < B; ++b) s += dh[((size_t)b * T + t) * C + c];
+  if (t < T) {  // rows b = 0, 1, ... in order, four loads in flight
+    int b = 0;
+    for (; b + 4 <= B; b += 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = dh[((size_t)(b + u) * T + t) * C + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; b < B; ++b) s += dh[((size_t)b * T + t) * C + c];
+  }
   float* p = dwpe + (size_t)t * C + c;
   *p = (beta != 0.f ? beta * *p : 0.f) + s;
 }

@@ -170,6 +170,28 @@ def test_emu_embedding_backward_zipf(L, B, T):
     close(dwpe, refp, 1e-6, "dwpe")
 
 
+@pytest.mark.parametrize("B,T,frac", [(16, 1024, 0.7), (20, 1000, 1.0)])
+def test_emu_embedding_backward_long_runs(L, B, T, frac):
+    """One id holding most (or all) of the positions: its run crosses more
+    than 256 chunks of 32 sorted entries, so the kernel that joins runs
+    across chunks has to search past its first window of chunk borders."""
+    C, V, bs = 64, 50257, 1024
+    M = B * T
+    rng = np.random.default_rng(M)
+    tok = rng.integers(0, V, M).astype(np.int32)
+    tok[rng.random(M) < frac] = 7
+    dh = rng.standard_normal((M, C)).astype(np.float32)
+    dwte0 = rng.standard_normal((50304, C)).astype(np.float32)
+    dwpe0 = rng.standard_normal((bs, C)).astype(np.float32)
+    dwte, dwpe = dwte0.copy(), dwpe0.copy()
+    ws = np.zeros(L.emu_embed_bwd_ws(M, C) // 4 + 64, np.float32)
+    assert L.emu_embed_bwd(ptr(tok), ptr(dh), ptr(dwte), ptr(dwpe), B, T, C, V, bs, 1.0, ptr(ws)) == 0
+    ref = dwte0.astype(np.float64)
+    np.add.at(ref, tok, dh.astype(np.float64))
+    close(dwte, ref, 1e-6, "dwte")
+    assert np.sum(tok == 7) > 256 * 32
+
+
 # ---------------------------------------------------------------------------- cross-entropy
 
 @pytest.mark.parametrize("V,Vp,ld,dt", [(50257, 50304, 50304, 1), (50257, 50257, 50304, 1), (50257, 50304, 50304, 2),
