@@ -27,6 +27,7 @@
 namespace gk {
 
 constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float RESCALE_LOG2 = 8.f;  // forward: stale-max slack before rescaling (probabilities < 2^8)
 constexpr int TILE = 64 * 64;  // one LDS tile, 16-bit elements
 
 // LDS tiles are 64 rows of 64 16-bit values (128-byte rows, no padding);
@@ -137,38 +138,49 @@ __device__ __forceinline__ void attn_fwd_tile(const uint16_t* Ks, const uint16_t
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s[kb] = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s[kb]);
+  // Raw scores (masked ones -inf); the running max m_i is in log2 units.
+  // It is raised only when the tile's max exceeds it by more than
+  // RESCALE_LOG2: otherwise the tile's probabilities are taken against the
+  // stale max (so they stay below 2^RESCALE_LOG2) and the accumulator needs
+  // no rescaling, which would otherwise cost a multiply and two register
+  // moves per accumulator element every tile.  O = oacc / l and
+  // lse = m_i + log2 l are unchanged in exact arithmetic.
   const bool diag = k0 + 63 > qw0;  // tile reaches past the wave's first query
+  if (diag) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key > q || key >= T) s[kb][e] = -INFINITY;
+      }
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = s[kb][e] * sl2;
-      if (diag) {
-        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (key > q || key >= T) v = -INFINITY;
-      }
-      s[kb][e] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(m_i, mx);
-  const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[kb][e], s[kb][e + 1]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // lanes l and l + 32 hold one query
+  const float mxs = mx * sl2;
+  if (mxs > m_i + RESCALE_LOG2) {  // always on the first tile (m_i = -inf)
+    const float alpha = __builtin_amdgcn_exp2f(m_i - mxs);
+    l_i *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    m_i = mxs;
+  }
   float ps = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float pv = __builtin_amdgcn_exp2f(s[kb][e] - m_new);
+      float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, -m_i));
       s[kb][e] = pv;
       ps += pv;
     }
-  l_i = l_i * alpha + ps;
-  m_i = m_new;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+  l_i += ps;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v8 pb = pack_slots<TE>(s[j >> 1], j & 1);

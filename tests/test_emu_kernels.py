@@ -356,6 +356,34 @@ def test_emu_flash_attention_forward_backward(L, B, T, H, dt):
         close(g, r, 2 ** -5, name)
 
 
+def test_emu_attention_forward_rising_scores(L):
+    """Scores that rise along the keys (q and k aligned, k growing with its
+    position) push every query's running max up by more than 2^8 per key
+    tile, so the forward's deferred rescaling runs on most tiles instead of
+    only the first; O and the log-sum-exp against the oracle."""
+    B, T, H, hd = 1, 300, 1, 64
+    C = H * hd
+    rng = np.random.default_rng(5)
+    u = np.ones(hd) / 8.0
+    pos = np.arange(T)[:, None] / T
+    q = 16.0 * u[None, :] + 0.1 * rng.standard_normal((T, hd))
+    k = 16.0 * pos * u[None, :] + 0.1 * rng.standard_normal((T, hd))
+    v = rng.standard_normal((T, hd))
+    qkv = bf16(np.concatenate([q, k, v], axis=1))
+    o = torch.zeros((B * T, C), dtype=torch.bfloat16)
+    lse = np.zeros(B * H * T, np.float32)
+    assert L.emu_attn_fwd(ptr(qkv), ptr(o), ptr(lse), B, T, H, hd, 1) == 0
+    q64 = f64(qkv).reshape(B, T, 3, H, hd).transpose(2, 0, 3, 1, 4)
+    oref = O.causal_attention_fwd(q64[0], q64[1], q64[2], np.float64)
+    close(f64(o).reshape(B, T, H, hd).transpose(0, 2, 1, 3), oref, 2 ** -6, "o")
+    sc = np.matmul(q64[0], np.swapaxes(q64[1], -1, -2)) / np.sqrt(hd)
+    sc[..., np.triu(np.ones((T, T), bool), 1)] = -np.inf
+    m = sc.max(-1)
+    assert (m[0, 0, -1] - m[0, 0, 64]) / np.log(2.0) > 8 * 3  # the max climbs by more than 8 per tile
+    lse_ref = (np.log(np.exp(sc - m[..., None]).sum(-1)) + m) / np.log(2.0)
+    close(lse.reshape(B, H, T), lse_ref, 1e-5, "lse (log2)")
+
+
 # ---------------------------------------------------------------------------- fp32 matrix-core GEMMs
 
 @pytest.mark.parametrize("M,N,K,at,bt,epi", [
