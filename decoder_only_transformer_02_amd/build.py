@@ -21,6 +21,13 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgpt2mi.so")
 SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "decode.hip", "engine.hip"]
 ARCH = "gfx950"
+# Per-source code generation options.  The attention kernels keep their
+# MFMA accumulators and results in ordinary VGPRs: by default the compiler
+# put them in AGPRs and copied them to VGPRs and back every key tile for
+# the softmax (272 accumulator moves in the forward's loop, 192 in dQ's),
+# and dQ fits three waves per SIMD instead of two this way.  The GEMM tiles
+# need the AGPRs for capacity and keep the default.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -62,7 +69,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *flags(), "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *flags(), *EXTRA.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -23,7 +23,7 @@ HOT = ["k_gemm_nt", "k_gemm_tn", "k_gemm_f32m", "k_splitk_reduce", "k_attn_fwd64
 FLOORS = [
     ("k_xentIDF16bLi25E", 3, "one row per block held in registers: needs rows in flight"),
     ("k_attn_fwd64", 3, "the softmax of one wave overlaps the MFMA of another"),
-    ("k_attn_dq64", 2, ""),
+    ("k_attn_dq64", 3, "with its MFMA results in VGPRs (attention.hip's build option)"),
     ("k_attn_dkv64", 2, ""),
     ("k_ln_fwdIDF16bLi4E", 4, "its grid puts four waves on every SIMD"),
     ("k_ln_bwdIDF16bLi4E", 2, "its grid puts two waves on every SIMD"),
@@ -72,3 +72,12 @@ def test_occupancy_floors(report, part, floor, why):
     assert ks, part
     for k, v in ks.items():
         assert v["occupancy"] >= floor, (k, v, why)
+
+
+def test_attention_keeps_mfma_results_in_vgprs(report):
+    """The attention kernels are built with their MFMA results in VGPRs, so
+    no accumulator registers are allocated (the softmax would otherwise
+    copy them back and forth every key tile)."""
+    for part in ("k_attn_fwd64", "k_attn_dq64", "k_attn_dkv64"):
+        for k, v in _match(report, part).items():
+            assert v.get("agpr", 0) == 0, (k, v)
