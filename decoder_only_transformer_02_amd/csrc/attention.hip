@@ -200,7 +200,10 @@ __global__ __launch_bounds__(256) void k_attn_fwd64(const TE* __restrict__ qkv,
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // heavy blocks first
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index through readfirstlane: the compiler then knows it (and
+  // the tile tests built from it) to be uniform across the wave and keeps
+  // those tests as scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, g = lane >> 5;
   const int q = q0 + 32 * w + fr;
   const TE* base = qkv + (size_t)b * T * ld;
@@ -329,13 +332,16 @@ __device__ __forceinline__ void attn_dq_tile(const uint16_t* Ks, const uint16_t*
       s = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s);
       dp = mfma(lds_row<TE>(Vs, kb * 32 + fr, 2 * ks + g), dof[ks], dp);
     }
+    if (diag) {  // masked scores to -inf: their probability comes out as 0
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key > q || key >= T) s[e] = -INFINITY;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float p = __builtin_amdgcn_exp2f(s[e] * sl2 - lq);
-      if (diag) {
-        int key = k0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (key > q || key >= T) p = 0.f;
-      }
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lq));
       s[e] = p * (dp[e] - Dq);  // dS^T
     }
 #pragma unroll
@@ -364,7 +370,10 @@ __global__ __launch_bounds__(256) void k_attn_dq64(const TE* __restrict__ qkv, c
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index through readfirstlane: the compiler then knows it (and
+  // the tile tests built from it) to be uniform across the wave and keeps
+  // those tests as scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, g = lane >> 5;
   const int q = q0 + 32 * w + fr;
   const TE* base = qkv + (size_t)b * T * ld;
@@ -452,6 +461,13 @@ __device__ __forceinline__ void attn_dkv_tile(const uint16_t* Qs, const uint16_t
       s = mfma(lds_row<TE>(Qs, qb * 32 + fr, 2 * ks + g), kf[ks], s);
       dp = mfma(lds_row<TE>(Os, qb * 32 + fr, 2 * ks + g), vf[ks], dp);
     }
+    if (diag) {  // masked scores to -inf: their probability comes out as 0
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qq = q0 + qb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key > qq || qq >= T) s[e] = -INFINITY;
+      }
+    }
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       const int ql0 = qb * 32 + e4 * 8 + g * 4;
@@ -461,11 +477,7 @@ __device__ __forceinline__ void attn_dkv_tile(const uint16_t* Qs, const uint16_t
 #pragma unroll
       for (int e1 = 0; e1 < 4; ++e1) {
         const int e = e4 * 4 + e1;
-        float p = __builtin_amdgcn_exp2f(s[e] * sl2 - Lr[e1]);
-        if (diag) {
-          int qq = q0 + ql0 + e1;
-          if (key > qq || qq >= T) p = 0.f;
-        }
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -Lr[e1]));
         s[e] = p;
         dp[e] = p * (dp[e] - Dr[e1]);
       }
@@ -498,7 +510,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int C = H * 64, ld = 3 * C;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int k0 = blockIdx.x * 128;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index through readfirstlane: the compiler then knows it (and
+  // the tile tests built from it) to be uniform across the wave and keeps
+  // those tests as scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, g = lane >> 5;
   const int key = k0 + 32 * w + fr;
   const TE* base = qkv + (size_t)b * T * ld;

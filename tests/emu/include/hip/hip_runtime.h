@@ -186,6 +186,34 @@ T shfl_idx(T v, int src, int width) {
   return o;
 }
 
+// v_readfirstlane: the first active lane's value.  The kernels use it only
+// to tell the compiler that a value is the same on every lane, so the
+// emulator also checks that it is.
+inline void rfl_fn(void*) {
+  int first = 0;
+  bool have = false;
+  for (int l = 0; l < 64; ++l) {
+    const void* p = lane_in(l);
+    if (!p) continue;
+    int v;
+    std::memcpy(&v, p, sizeof(v));
+    if (!have) {
+      first = v;
+      have = true;
+    } else if (v != first) {
+      std::fprintf(stderr, "emu: readfirstlane of a value that differs across the wave\n");
+      std::abort();
+    }
+  }
+  for (int l = 0; l < 64; ++l) std::memcpy(lane_out(l), &first, sizeof(first));
+}
+inline int readfirstlane(int v) {
+  void* r = wave_collective(1200, &v, sizeof(v), rfl_fn, nullptr);
+  int o;
+  std::memcpy(&o, r, sizeof(o));
+  return o;
+}
+
 // generic launch: runs the whole grid before returning (streams are
 // synchronous in the emulator)
 typedef void (*BlockThunk)(void* args);
@@ -234,6 +262,7 @@ inline void __syncthreads() { ::emu::syncthreads(); }
 #define __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, x, y, z) ::emu::mfma_32x32x2_f32(a, b, c)
 #define __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, x, y, z) ::emu::mfma_32x32x16_f16(a, b, c)
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16_b64((const void*)(p))
+#define __builtin_amdgcn_readfirstlane(v) ::emu::readfirstlane((int)(v))
 #define __builtin_amdgcn_make_buffer_rsrc(b, s, n, f) ::emu::make_rsrc(b, s, n, f)
 #define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, sz, vo, so, of, ax) \
   ::emu::buffer_load_lds(r, (void*)(l), sz, vo, so, of, ax)
