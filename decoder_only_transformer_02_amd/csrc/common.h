@@ -94,23 +94,23 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// tanh from its exponential form, tanh(x) = 1 - 2 / (exp(2x) + 1), with the
-// hardware exp2 and reciprocal; saturates correctly to +-1.
-__device__ __forceinline__ float fast_tanh(float x) {
-  float e = __builtin_amdgcn_exp2f(x * 2.8853900817779268f);  // 2 / ln 2
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// tanh-GELU and its derivative (Hendrycks & Gimpel), fp32, in the logistic
+// form: 0.5 (1 + tanh(z / 2)) = 1 / (1 + exp(-z)) with z = 2k (u + a u^3),
+// so gelu(u) = u s and gelu'(u) = s (1 + u (1 - s) z'(u)), s = 1 / (1 +
+// exp(-z)), z' = 2k (1 + 3a u^2).  One exp2 and one reciprocal each, and
+// the cubic folded into fused multiply-adds: these run once per element of
+// the MLP's widest GEMM outputs, inside the GEMM epilogue.
+__device__ __forceinline__ float gelu_sigmoid_of(float u) {
+  const float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2k / ln 2
+  const float c1 = c0 * 0.044715f;
+  const float x = u * fmaf(c1, u * u, c0);  // -z / ln 2
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
-
-// tanh-GELU and its derivative (Hendrycks & Gimpel), fp32.
-__device__ __forceinline__ float gelu_tanh_f(float u) {
-  const float k = 0.7978845608028654f, a = 0.044715f;
-  float t = fast_tanh(k * (u + a * u * u * u));
-  return 0.5f * u * (1.0f + t);
-}
+__device__ __forceinline__ float gelu_tanh_f(float u) { return u * gelu_sigmoid_of(u); }
 __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
-  const float k = 0.7978845608028654f, a = 0.044715f;
-  float t = fast_tanh(k * (u + a * u * u * u));
-  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * k * (1.0f + 3.0f * a * u * u);
+  const float d0 = 2.0f * 0.7978845608028654f, d1 = d0 * 3.0f * 0.044715f;  // z' = d0 + d1 u^2
+  const float s = gelu_sigmoid_of(u);
+  return s * fmaf(u * (1.0f - s), fmaf(d1, u * u, d0), 1.0f);
 }
 
 __host__ __device__ __forceinline__ int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
