@@ -118,6 +118,45 @@ __device__ __forceinline__ void epi_store4(const GP& p, int r, int c, float v0, 
   }
 }
 
+// The 16-bit epilogues of a tile that lies wholly inside the output: no
+// bounds tests, and the bias of columns c..c+3 passed in (loaded once for
+// all the row fragments that share those columns), so the compiler can keep
+// one row address per fragment and fold the column offsets into the stores.
+template <int EPI, typename TE>
+__device__ __forceinline__ void epi_store4_full(const GP& p, int r, int c, float4 b, float v0, float v1,
+                                                float v2, float v3) {
+  const size_t o = (size_t)r * p.ldo + c;
+  if constexpr (EPI == EPI_STORE) {
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(p.alpha * v0 + b.x, p.alpha * v1 + b.y),
+                                             H16<TE>::pack2(p.alpha * v2 + b.z, p.alpha * v3 + b.w));
+  } else if constexpr (EPI == EPI_LOGITS) {
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(v0, v1), H16<TE>::pack2(v2, v3));
+  } else if constexpr (EPI == EPI_GELU) {
+    float u0 = v0 + b.x, u1 = v1 + b.y, u2 = v2 + b.z, u3 = v3 + b.w;
+    *(uint2*)((TE*)p.out + o) = make_uint2(H16<TE>::pack2(u0, u1), H16<TE>::pack2(u2, u3));
+    *(uint2*)((TE*)p.out2 + o) = make_uint2(H16<TE>::pack2(gelu_tanh_f(u0), gelu_tanh_f(u1)),
+                                              H16<TE>::pack2(gelu_tanh_f(u2), gelu_tanh_f(u3)));
+  } else if constexpr (EPI == EPI_RESID) {
+    float4 x = *(const float4*)((const float*)p.aux + o);
+    *(float4*)((float*)p.out + o) = make_float4(x.x + v0 + b.x, x.y + v1 + b.y, x.z + v2 + b.z,
+                                                x.w + v3 + b.w);
+  } else if constexpr (EPI == EPI_DGELU) {
+    uint2 uu = *(const uint2*)((const TE*)p.aux + o);
+    float u0 = H16<TE>::lo(uu.x), u1 = H16<TE>::hi(uu.x);
+    float u2 = H16<TE>::lo(uu.y), u3 = H16<TE>::hi(uu.y);
+    *(uint2*)((TE*)p.out + o) =
+        make_uint2(H16<TE>::pack2(v0 * gelu_tanh_grad_f(u0), v1 * gelu_tanh_grad_f(u1)),
+                   H16<TE>::pack2(v2 * gelu_tanh_grad_f(u2), v3 * gelu_tanh_grad_f(u3)));
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ float4 epi_bias4(const GP& p, int c) {
+  if constexpr (EPI == EPI_GELU || EPI == EPI_RESID) return *(const float4*)(p.bias + c);
+  if constexpr (EPI == EPI_STORE) return p.bias ? *(const float4*)(p.bias + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // ------------------------------------------------------------------ 16-bit MFMA kernel
 constexpr int BK = 64;       // K tile (16-bit elements)
 constexpr int LDS_LD = 72;   // padded LDS row (elements): 144 B, 16-byte aligned
@@ -550,20 +589,37 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
     int tm, tn;
     grouped_coords(tile_pid(round, G), nm, nn, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    if (m0 + BM <= p.M && n0 + BN <= p.N) {  // whole tile inside the output
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+          const float4 b = epi_bias4<EPI>(p, c);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            epi_store4_full<EPI, TE>(p, m0 + wm + i * 32 + fr, c, b, acc[i][j][e4 * 4 + 0],
+                                     acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            int r = m0 + wm + i * 32 + fr;
+            int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+            epi_store4<EPI, TE>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                                acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+          }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          int r = m0 + wm + i * 32 + fr;
-          int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
-          epi_store4<EPI, TE>(p, r, c, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
-                              acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
-        }
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-      }
   }
 }
 
