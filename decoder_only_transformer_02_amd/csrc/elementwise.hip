@@ -90,13 +90,18 @@ hipError_t embed_fwd(const int32_t* tok, const float* wte, const float* wpe, flo
 }
 
 // ------------------------------------------------------------------ LayerNorm forward
+// FULL: C is exactly 256 NV (each lane's NV float4 columns all exist), so the
+// per-chunk column tests go away; other widths take NV = 4 with the tests.
+template <bool FULL>
+__device__ __forceinline__ bool ln_in(int c, int C) { return FULL || c < C; }
+
 // y = (x - mean) * rstd * w + b, biased variance, one wave per row.  The row
 // stays in registers (NV float4 per lane, C <= 256 * NV).  Each wave walks
 // the rows wave_id, wave_id + nwaves, ... with w and b held in registers
 // and the next row's loads issued before the current row's reductions.
 constexpr int LN_FWD_BLOCKS = 1024;
 
-template <typename TO, int NV>
+template <typename TO, int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
                                                 const float* __restrict__ w,
                                                 const float* __restrict__ b, TO* __restrict__ y,
@@ -110,9 +115,9 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int c = (lane + i * 64) * 4;
-    ww[i] = c < C ? *(const float4*)(w + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    bb[i] = c < C ? *(const float4*)(b + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    v[i] = c < C ? *(const float4*)(x + (size_t)row * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ww[i] = ln_in<FULL>(c, C) ? *(const float4*)(w + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    bb[i] = ln_in<FULL>(c, C) ? *(const float4*)(b + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = ln_in<FULL>(c, C) ? *(const float4*)(x + (size_t)row * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const float invC = 1.0f / (float)C;
   for (; row < M; row += stride) {
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         int c = (lane + i * 64) * 4;
-        vn[i] = c < C ? *(const float4*)(x + (size_t)(row + stride) * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vn[i] = ln_in<FULL>(c, C) ? *(const float4*)(x + (size_t)(row + stride) * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     float s = 0.f;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
-      if (c < C) {
+      if (ln_in<FULL>(c, C)) {
         float a0 = v[i].x - mu, a1 = v[i].y - mu, a2 = v[i].z - mu, a3 = v[i].w - mu;
         q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
       }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
-      if (c < C)
+      if (ln_in<FULL>(c, C))
         Vec4<TO>::store(yr + c, (v[i].x - mu) * rs * ww[i].x + bb[i].x, (v[i].y - mu) * rs * ww[i].y + bb[i].y,
                         (v[i].z - mu) * rs * ww[i].z + bb[i].z, (v[i].w - mu) * rs * ww[i].w + bb[i].w);
     }
@@ -158,16 +163,29 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
   }
 }
 
+template <typename TO, int NV, bool FULL>
+static void ln_fwd_launch(int g, hipStream_t st, const float* x, const float* w, const float* b, void* y,
+                          float* mean, float* rstd, int M, int C, float eps) {
+  k_ln_fwd<TO, NV, FULL><<<g, 256, 0, st>>>(x, w, b, (TO*)y, mean, rstd, M, C, eps);
+}
+// the exact-width variant for C = 256, 512, 768, 1024, else NV = 4 with tests
+template <typename TO>
+static void ln_fwd_width(int g, hipStream_t st, const float* x, const float* w, const float* b, void* y,
+                         float* mean, float* rstd, int M, int C, float eps) {
+  if (C == 256) ln_fwd_launch<TO, 1, true>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else if (C == 512) ln_fwd_launch<TO, 2, true>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else if (C == 768) ln_fwd_launch<TO, 3, true>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else if (C == 1024) ln_fwd_launch<TO, 4, true>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else ln_fwd_launch<TO, 4, false>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+}
+
 hipError_t ln_fwd(const float* x, const float* w, const float* b, void* y, int dt, float* mean,
                   float* rstd, int M, int C, float eps, hipStream_t st) {
   if (C % 4 || C > 1024) return hipErrorInvalidValue;
   int g = min(cdiv(M, 4), LN_FWD_BLOCKS);
-  if (dt == ACT_BF16)
-    k_ln_fwd<bf16, 4><<<g, 256, 0, st>>>(x, w, b, (bf16*)y, mean, rstd, M, C, eps);
-  else if (dt == ACT_F16)
-    k_ln_fwd<f16, 4><<<g, 256, 0, st>>>(x, w, b, (f16*)y, mean, rstd, M, C, eps);
-  else
-    k_ln_fwd<float, 4><<<g, 256, 0, st>>>(x, w, b, (float*)y, mean, rstd, M, C, eps);
+  if (dt == ACT_BF16) ln_fwd_width<bf16>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else if (dt == ACT_F16) ln_fwd_width<f16>(g, st, x, w, b, y, mean, rstd, M, C, eps);
+  else ln_fwd_width<float>(g, st, x, w, b, y, mean, rstd, M, C, eps);
   return hipGetLastError();
 }
 
@@ -182,7 +200,7 @@ int ln_bwd_blocks(int M) {
   return nb < 512 ? nb : 512;
 }
 
-template <typename TA, int NV>
+template <typename TA, int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
                                                 const float* __restrict__ mean,
                                                 const float* __restrict__ rstd,
@@ -197,7 +215,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int c = (lane + i * 64) * 4;
-    wr[i] = c < C ? *(const float4*)(w + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    wr[i] = ln_in<FULL>(c, C) ? *(const float4*)(w + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     dwa[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     dba[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
-      if (c < C) {
+      if (ln_in<FULL>(c, C)) {
         xo[i] = *(const float4*)(x + (size_t)r * C + c);
         d_o[i] = Vec4<TA>::load_raw(dy + (size_t)r * C + c);
       }
@@ -236,7 +254,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         int c = (lane + i * 64) * 4;
-        if (c < C) prev[i] = *(const float4*)(dr + c);
+        if (ln_in<FULL>(c, C)) prev[i] = *(const float4*)(dr + c);
       }
     }
     float4 xh[NV], gg[NV];
@@ -244,7 +262,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
-      if (c < C) {
+      if (ln_in<FULL>(c, C)) {
         const float4 xv = xc[i];
         const float4 d = Vec4<TA>::cvt(dc[i]);
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int c = (lane + i * 64) * 4;
-      if (c < C) {
+      if (ln_in<FULL>(c, C)) {
         float4 o = make_float4(rs * (gg[i].x - mg - xh[i].x * mgx), rs * (gg[i].y - mg - xh[i].y * mgx),
                                rs * (gg[i].z - mg - xh[i].z * mgx), rs * (gg[i].w - mg - xh[i].w * mgx));
         if (accum) {
@@ -283,7 +301,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int c = (lane + i * 64) * 4;
-    if (c < C) {
+    if (ln_in<FULL>(c, C)) {
       *(float4*)&red[0][wv][c] = dwa[i];
       *(float4*)&red[1][wv][c] = dba[i];
     }
@@ -297,21 +315,33 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
   }
 }
 
+template <typename TA, int NV, bool FULL>
+static void ln_bwd_launch(int nb, hipStream_t st, const float* x, const float* mean, const float* rstd,
+                          const float* w, const void* dy, float* dres, void* dres_act, bool accum, float* part,
+                          int M, int C, int rpb) {
+  k_ln_bwd<TA, NV, FULL><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const TA*)dy, dres, (TA*)dres_act, accum, part,
+                                             M, C, rpb);
+}
+template <typename TA>
+static void ln_bwd_width(int nb, hipStream_t st, const float* x, const float* mean, const float* rstd,
+                         const float* w, const void* dy, float* dres, void* dres_act, bool accum, float* part,
+                         int M, int C, int rpb) {
+  if (C == 256) ln_bwd_launch<TA, 1, true>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else if (C == 512) ln_bwd_launch<TA, 2, true>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else if (C == 768) ln_bwd_launch<TA, 3, true>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else if (C == 1024) ln_bwd_launch<TA, 4, true>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else ln_bwd_launch<TA, 4, false>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+}
+
 hipError_t ln_bwd(const float* x, const float* mean, const float* rstd, const float* w,
                   const void* dy, int dt, float* dres, void* dres_act, bool accum,
                   float* part, int M, int C, hipStream_t st) {
   if (C % 4 || C > 1024) return hipErrorInvalidValue;
   int nb = ln_bwd_blocks(M);
   int rpb = cdiv(M, nb);
-  if (dt == ACT_BF16)
-    k_ln_bwd<bf16, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const bf16*)dy, dres, (bf16*)dres_act,
-                                          accum, part, M, C, rpb);
-  else if (dt == ACT_F16)
-    k_ln_bwd<f16, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const f16*)dy, dres, (f16*)dres_act,
-                                         accum, part, M, C, rpb);
-  else
-    k_ln_bwd<float, 4><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const float*)dy, dres,
-                                           (float*)dres_act, accum, part, M, C, rpb);
+  if (dt == ACT_BF16) ln_bwd_width<bf16>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else if (dt == ACT_F16) ln_bwd_width<f16>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
+  else ln_bwd_width<float>(nb, st, x, mean, rstd, w, dy, dres, dres_act, accum, part, M, C, rpb);
   return hipGetLastError();
 }
 
