@@ -5,10 +5,11 @@
 // j <= i.  q, k, v are read in place from the packed qkv rows [B*T, 3C].
 //
 // head_dim 64, 16-bit operands (bf16 or fp16): matrix-core kernels.  Each
-// wave owns 32 queries (or
-// 32 keys in the dK/dV kernel) as the 32-wide MFMA column; K/V (or Q/dO)
-// tiles of 64 rows are staged in LDS, double-buffered (one barrier per
-// tile), and shared by the 4 waves of a block.  Tiles keep the row-major
+// wave owns 32 queries (or 32 keys in the dK/dV kernel) as the 32-wide MFMA
+// column; K/V (or Q/dO) tiles of 64 rows are staged in LDS, double-buffered
+// (one barrier per tile), and shared by the 4 waves of a block.  This file
+// is compiled with the MFMA operands and results in VGPRs (build.py): the
+// softmax works on them directly instead of copying them out of AGPRs.  Tiles keep the row-major
 // [row][d] layout; operands that need the contraction over rows (P V,
 // dS K, P^T dO, dS^T Q) are built with the gfx950 LDS transpose read.
 // Scores are formed transposed (S^T = K Q^T) so that a lane holds 16 scores
