@@ -58,9 +58,7 @@ def class_work(p, B, T, n_params):
     per causal score (QK^T and PV) forward, twice that backward (recompute
     not credited).  LayerNorm forward (6C+8) and backward (14C+8) bytes per
     token over 2L+1 LayerNorms; cross-entropy (4 Vp + 8) bytes per token;
-    gradient norm 4 bytes and AdamW 30 bytes per parameter; the transposed
-    weight copies 4 bytes (one 16-bit read, one write) per GEMM-weight
-    element."""
+    gradient norm 4 bytes and AdamW 30 bytes per parameter."""
     L, C, H, Vp = p["n_layer"], p["n_embd"], p["n_head"], p["padded_vocab"]
     M = B * T
     hd = C // H
@@ -77,7 +75,6 @@ def class_work(p, B, T, n_params):
         "xent": ("hbm", M * (4 * Vp + 8), "byte"),
         "norm": ("hbm", 4 * n_params, "byte"),
         "adamw": ("hbm", 30 * n_params, "byte"),
-        "transpose": ("hbm", 4 * (Vp * C + L * 12 * C * C), "byte"),
     }
 
 
@@ -213,7 +210,7 @@ def main():
     print("per-class kernel timing", file=sys.stderr, flush=True)
     kernels = {}
     for cls in ("lmhead_fwd", "gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "xent", "norm", "adamw",
-                "transpose", "embed", "colsum"):
+                "embed"):
         c_ms, c_n = r.class_ms(cls)
         k = {"ms_per_step": round(c_ms, 4), "launches_per_step": c_n}
         if cls in work:

@@ -50,8 +50,9 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 
 // The two 16-bit storage types of the matrix-core path, bf16 and fp16 (IEEE
 // half): the 8-element MFMA operand vector, the 32x32x16 matrix instruction
-// with fp32 accumulation, and packing of two floats into one dword (low
-// half = first, round to nearest even) and back.
+// with fp32 accumulation, packing of two floats into one dword (low half =
+// first, round to nearest even) and back, and acc + lo + hi of one dword in
+// a single instruction (v_dot2 against a pair of ones).
 template <typename T> struct H16;
 template <> struct H16<bf16> {
   typedef bf16x8 v8;
@@ -61,6 +62,10 @@ template <> struct H16<bf16> {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf2(a, b); }
   static __device__ __forceinline__ float lo(uint32_t u) { return bfbits2f(u & 0xffffu); }
   static __device__ __forceinline__ float hi(uint32_t u) { return bfbits2f(u >> 16); }
+  static __device__ __forceinline__ float add_pair(uint32_t u, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+  }
 };
 template <> struct H16<f16> {
   typedef f16x8 v8;
@@ -75,6 +80,9 @@ template <> struct H16<f16> {
   }
   static __device__ __forceinline__ float lo(uint32_t u) { return (float)__builtin_bit_cast(f16, (uint16_t)(u & 0xffffu)); }
   static __device__ __forceinline__ float hi(uint32_t u) { return (float)__builtin_bit_cast(f16, (uint16_t)(u >> 16)); }
+  static __device__ __forceinline__ float add_pair(uint32_t u, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
 };
 
 // Wavefront (64 lanes) all-reduce.

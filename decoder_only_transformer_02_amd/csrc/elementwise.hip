@@ -1196,58 +1196,6 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow,
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ weight transposes
-// The transposed 16-bit copies of all GEMM weights in one launch: job j
-// transposes the [R, C] matrix at src_base + src into dst_base + dst (row
-// stride ldt) and owns the 64 x 64 tiles [first_tile, first_tile +
-// ceil(R/64) ceil(C/64)), column tiles fastest; block b finds its job by a
-// binary search over first_tile.  Each tile goes through LDS so both the
-// reads and the writes are row-contiguous.
-__global__ __launch_bounds__(256) void k_transpose_jobs(const uint16_t* __restrict__ src_base,
-                                                        uint16_t* __restrict__ dst_base,
-                                                        const TransposeJob* __restrict__ jobs, int njobs) {
-  __shared__ uint16_t t[64][66];
-  const int blk = blockIdx.x;
-  int lo = 0, hi = njobs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (jobs[mid].first_tile <= blk) lo = mid;
-    else hi = mid - 1;
-  }
-  const TransposeJob J = jobs[lo];
-  const uint16_t* src = src_base + J.src;
-  uint16_t* dst = dst_base + J.dst;
-  const int R = J.R, C = J.C, ldt = J.ldt;
-  const int tile = blk - J.first_tile, ntc = cdiv(C, 64);
-  const int r0 = (tile / ntc) * 64, c0 = (tile % ntc) * 64;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int i = ty; i < 64; i += 8) {
-    int r = r0 + i, c = c0 + 2 * tx;
-    uint32_t v = 0;
-    if (r < R && c + 1 < C) v = *(const uint32_t*)(src + (size_t)r * C + c);
-    else if (r < R && c < C) v = src[(size_t)r * C + c];
-    t[i][2 * tx] = (uint16_t)(v & 0xffffu);
-    t[i][2 * tx + 1] = (uint16_t)(v >> 16);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 8) {
-    int c = c0 + i, r = r0 + 2 * tx;
-    if (c >= C) continue;
-    if (r + 1 < R) {
-      *(uint32_t*)(dst + (size_t)c * ldt + r) = (uint32_t)t[2 * tx][i] | ((uint32_t)t[2 * tx + 1][i] << 16);
-    } else if (r < R) {
-      dst[(size_t)c * ldt + r] = t[2 * tx][i];
-    }
-  }
-}
-
-hipError_t transpose_jobs(const uint16_t* src_base, uint16_t* dst_base, const TransposeJob* jobs, int njobs,
-                          int total_tiles, hipStream_t st) {
-  if (njobs < 1 || total_tiles < 1) return hipSuccess;
-  k_transpose_jobs<<<total_tiles, 256, 0, st>>>(src_base, dst_base, jobs, njobs);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ misc
 __global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

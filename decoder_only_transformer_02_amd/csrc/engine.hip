@@ -136,7 +136,6 @@ struct gpt2_ctx {
   std::vector<ParamSpec> specs;
   std::vector<size_t> poff;  // element offset of each parameter in the flat arrays
   size_t nflat = 0;          // flat array length (padded)
-  size_t nflat_t = 0;        // transposed-copy array length
   int L, H, C, hd, V, Vp, ldl, maxM;
   bool h16;     // 16-bit activations and GEMM operands (bf16 or fp16)
   int dt;       // activation type (gk::ActType)
@@ -147,12 +146,6 @@ struct gpt2_ctx {
 
   float *params, *grads, *am, *av;
   uint16_t* shadow;
-  uint16_t* shadow_t;              // transposed 16-bit copies of the GEMM weights
-  std::vector<size_t> toff;        // element offset of each transposed copy (or -1)
-  std::vector<int> tld;            // its row stride
-  std::vector<gk::TransposeJob> tjobs;  // one per transposed copy (host copy of the table)
-  gk::TransposeJob* tjobs_dev = nullptr;
-  int ttiles = 0;
   std::vector<float*> h, mean, rstd, lse;
   std::vector<void*> ln, qkv, att, fcu, fcg;
   void* logits;
@@ -185,7 +178,6 @@ struct gpt2_ctx {
   const void* W(int j) const {  // GEMM operand copy of a weight
     return h16 ? (const void*)(shadow + poff[j]) : (const void*)(params + poff[j]);
   }
-  const void* Wt(int j) const { return shadow_t + toff[j]; }  // [in, out] (16-bit only)
   int li(int l, int k) const { return 2 + 12 * l + k; }  // parameter index in layer l
   void* act(void* base, size_t elems_off) const { return (char*)base + elems_off * act_es; }
 };
@@ -253,32 +245,6 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
   size_t o_par = pl.raw(nflat * 4, "parameters"), o_grad = pl.raw(nflat * 4, "gradients");
   size_t o_m = pl.raw(nflat * 4, "adam_m"), o_v = pl.raw(nflat * 4, "adam_v");
   size_t o_sh = bf ? pl.raw(nflat * 2, "16-bit weight copies") : 0;
-  std::vector<size_t> toff(specs.size(), (size_t)-1);
-  std::vector<int> tld(specs.size(), 0);
-  size_t nt = 0;
-  for (size_t j = 0; j < specs.size(); ++j) {
-    if (!bf || !specs[j].gemm_weight) continue;
-    int ld = (int)(((specs[j].rows + 63) / 64) * 64);   // transposed rows are the old columns
-    toff[j] = nt;
-    tld[j] = ld;
-    nt += (size_t)specs[j].cols * ld;
-  }
-  size_t o_sht = bf ? pl.raw(nt * 2 + 256, "transposed 16-bit weight copies") : 0;
-  std::vector<gk::TransposeJob> tjobs;
-  int ttiles = 0;
-  for (size_t j = 0; j < specs.size(); ++j) {
-    if (toff[j] == (size_t)-1) continue;
-    gk::TransposeJob jb;
-    jb.src = poff[j];
-    jb.dst = toff[j];
-    jb.R = (int32_t)specs[j].rows;
-    jb.C = (int32_t)specs[j].cols;
-    jb.ldt = tld[j];
-    jb.first_tile = ttiles;
-    ttiles += (int)(((specs[j].rows + 63) / 64) * ((specs[j].cols + 63) / 64));
-    tjobs.push_back(jb);
-  }
-  size_t o_tjobs = pl.raw(tjobs.size() * sizeof(gk::TransposeJob) + 8, "transpose job table");
   // tensor-table views of the flat arrays
   for (size_t j = 0; j < specs.size(); ++j) {
     auto& s = specs[j];
@@ -297,17 +263,6 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
       size_t es = k == 4 ? 2 : 4;
       t.offset = base[k] + poff[j] * es;
       t.bytes = s.numel() * es;
-      pl.out->push_back(t);
-    }
-    if (toff[j] != (size_t)-1) {  // transposed copy [in, ldt]: columns >= out are padding
-      t.name = "t16." + s.name;
-      t.kind = GPT2_K_SHADOW;
-      t.dtype = adt;
-      t.ndim = 2;
-      t.shape[0] = s.cols;
-      t.shape[1] = tld[j];
-      t.offset = o_sht + toff[j] * 2;
-      t.bytes = (size_t)s.cols * tld[j] * 2;
       pl.out->push_back(t);
     }
   }
@@ -369,13 +324,6 @@ size_t plan(const gpt2_config& c, gpt2_ctx* x) {
     x->params = (float*)(a + o_par); x->grads = (float*)(a + o_grad);
     x->am = (float*)(a + o_m); x->av = (float*)(a + o_v);
     x->shadow = bf ? (uint16_t*)(a + o_sh) : nullptr;
-    x->shadow_t = bf ? (uint16_t*)(a + o_sht) : nullptr;
-    x->toff = toff;
-    x->tld = tld;
-    x->tjobs = tjobs;
-    x->tjobs_dev = (gk::TransposeJob*)(a + o_tjobs);
-    x->ttiles = ttiles;
-    x->nflat_t = nt;
     for (int k = 0; k <= 2 * L; ++k) {
       x->h.push_back((float*)(a + o_h[k]));
       x->ln.push_back(a + o_ln[k]);
@@ -539,17 +487,24 @@ hipError_t ln_backward(gpt2_ctx* c, int k, int wj, const void* dy, bool accum, f
                                   beta, c->st);
 }
 
-hipError_t colsum_timed(gpt2_ctx* c, const void* X, int M, int N, int ldx, float* db, float beta) {
-  Timed t(c, GPT2_T_COLSUM);
-  return gk::colsum(X, c->dt, M, N, ldx, db, beta, c->col_part, c->st);
+// Weight gradient dW[out, in] (+)= dY^T X of a linear layer and, with
+// bias index bj >= 0, its bias gradient db (+)= column sums of dY, which the
+// GEMM forms from the dY tiles it stages.
+hipError_t wgrad(gpt2_ctx* c, int M, int n_out, int n_in, const void* dY, const void* X, int wj, int bj,
+                 float beta) {
+  GemmArgs g = gemm_args(c, n_out, n_in, M, dY, n_out, true, X, n_in, true, gk::EPI_WGRAD, c->G(wj), n_in);
+  g.beta = beta;
+  if (bj >= 0) {
+    g.dbias = c->G(bj);
+    g.colsum_ws = c->col_part;
+  }
+  return run_gemm(c, g);
 }
 
-// dX[M, in] = dY[M, out] W[out, in]: NT against the transposed copy in 16 bits,
-// NN (B transposed in memory) in fp32.
+// dX[M, in] = dY[M, out] W[out, in]: the weight (or its 16-bit copy) is read
+// in its own [out][in] layout, i.e. as B transposed in memory.
 GemmArgs dx_args(gpt2_ctx* c, int M, int n_in, int n_out, const void* dY, int ldy, int wj, int kind,
                  void* out, int ldo) {
-  if (c->h16)
-    return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->Wt(wj), c->tld[wj], false, kind, out, ldo);
   return gemm_args(c, M, n_in, n_out, dY, ldy, false, c->W(wj), n_in, true, kind, out, ldo);
 }
 
@@ -561,28 +516,16 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   GemmArgs g = dx_args(c, M, 4 * C, C, c->dres_act, C, c->li(l, 10), gk::EPI_DGELU, c->du, 4 * C);
   g.aux = c->fcu[l];
   KCHK(run_gemm(c, g));
-  g = gemm_args(c, C, 4 * C, M, c->dres_act, C, true, c->fcg[l], 4 * C, true, gk::EPI_WGRAD,
-                c->G(c->li(l, 10)), 4 * C);
-  g.beta = beta;
-  KCHK(run_gemm(c, g));
-  KCHK(colsum_timed(c, c->dres_act, M, C, C, c->G(c->li(l, 11)), beta));
+  KCHK(wgrad(c, M, C, 4 * C, c->dres_act, c->fcg[l], c->li(l, 10), c->li(l, 11), beta));
   // fc: da2 = du W_fc; dW_fc = du^T a2; db_fc = sum du
   g = dx_args(c, M, C, 4 * C, c->du, 4 * C, c->li(l, 8), gk::EPI_STORE, c->dA, C);
   KCHK(run_gemm(c, g));
-  g = gemm_args(c, 4 * C, C, M, c->du, 4 * C, true, c->ln[2 * l + 1], C, true, gk::EPI_WGRAD,
-                c->G(c->li(l, 8)), C);
-  g.beta = beta;
-  KCHK(run_gemm(c, g));
-  KCHK(colsum_timed(c, c->du, M, 4 * C, 4 * C, c->G(c->li(l, 9)), beta));
+  KCHK(wgrad(c, M, 4 * C, C, c->du, c->ln[2 * l + 1], c->li(l, 8), c->li(l, 9), beta));
   KCHK(ln_backward(c, 2 * l + 1, c->li(l, 6), c->dA, true, beta, M));
   // attention projection: do = dr W_proj; dW_proj = dr^T o; db_proj
   g = dx_args(c, M, C, C, c->dres_act, C, c->li(l, 4), gk::EPI_STORE, c->dattn, C);
   KCHK(run_gemm(c, g));
-  g = gemm_args(c, C, C, M, c->dres_act, C, true, c->att[l], C, true, gk::EPI_WGRAD,
-                c->G(c->li(l, 4)), C);
-  g.beta = beta;
-  KCHK(run_gemm(c, g));
-  KCHK(colsum_timed(c, c->dres_act, M, C, C, c->G(c->li(l, 5)), beta));
+  KCHK(wgrad(c, M, C, C, c->dres_act, c->att[l], c->li(l, 4), c->li(l, 5), beta));
   {
     Timed t(c, GPT2_T_ATTN_BWD);
     KCHK(gk::attn_bwd(c->qkv[l], c->att[l], c->dattn, c->lse[l], c->dqkv, c->attn_ws, B, T, c->H,
@@ -591,20 +534,9 @@ hipError_t bwd_layer(gpt2_ctx* c, int l, int M, int B, int T, float beta) {
   // qkv: da1 = dqkv W_qkv; dW_qkv = dqkv^T a1; db_qkv
   g = dx_args(c, M, C, 3 * C, c->dqkv, 3 * C, c->li(l, 2), gk::EPI_STORE, c->dA, C);
   KCHK(run_gemm(c, g));
-  g = gemm_args(c, 3 * C, C, M, c->dqkv, 3 * C, true, c->ln[2 * l], C, true, gk::EPI_WGRAD,
-                c->G(c->li(l, 2)), C);
-  g.beta = beta;
-  KCHK(run_gemm(c, g));
-  KCHK(colsum_timed(c, c->dqkv, M, 3 * C, 3 * C, c->G(c->li(l, 3)), beta));
+  KCHK(wgrad(c, M, 3 * C, C, c->dqkv, c->ln[2 * l], c->li(l, 2), c->li(l, 3), beta));
   KCHK(ln_backward(c, 2 * l, c->li(l, 0), c->dA, true, beta, M));
   return hipSuccess;
-}
-
-// Refreshes the transposed 16-bit copies from the 16-bit weight copies.
-hipError_t refresh_transposed(gpt2_ctx* c) {
-  if (!c->h16) return hipSuccess;
-  Timed t(c, GPT2_T_TRANSPOSE);
-  return gk::transpose_jobs(c->shadow, c->shadow_t, c->tjobs_dev, (int)c->tjobs.size(), c->ttiles, c->st);
 }
 
 // The forward schedule over the ids already in c->tok ([B, T] packed):
@@ -768,17 +700,12 @@ GPT2_API gpt2_status gpt2_create(const gpt2_config* cfg, uint64_t seed, void* d_
   for (const Guard& g : c->guards)
     if ((e = hipMemsetAsync(c->arena + g.offset, kGuardByte, kGuard, c->st))) return bail(e, "guards");
   if (c->h16 && (e = gk::to_h16(c->params, c->shadow, c->nflat, c->dt, c->st))) return bail(e, "16-bit copy");
-  if (c->h16 && (e = hipMemsetAsync(c->shadow_t, 0, c->nflat_t * 2, c->st))) return bail(e, "zero t");
-  if (c->h16 && (e = hipMemcpyAsync(c->tjobs_dev, c->tjobs.data(), c->tjobs.size() * sizeof(gk::TransposeJob),
-                                    hipMemcpyHostToDevice, c->st)))
-    return bail(e, "transpose job table");
   if (c->ls) {  // dynamic loss scale and its step counter
     c->ls_staging[0] = 65536.f;
     c->ls_staging[1] = 0.f;
     if ((e = hipMemcpyAsync(c->scal + 10, c->ls_staging, 8, hipMemcpyHostToDevice, c->st)))
       return bail(e, "loss scale");
   }
-  if ((e = refresh_transposed(c))) return bail(e, "transposed copies");
   // AdamW chunk table
   std::vector<gk::AdamChunk> ch;
   const size_t CH = 16384;
@@ -976,7 +903,6 @@ GPT2_API gpt2_status gpt2_step(gpt2_ctx* c, float lr, float clip, float* h_grad_
     HIPCHK(c, gk::adamw(c->params, c->grads, c->am, c->av, c->shadow, c->dt, c->chunks, c->nchunks, c->scal,
                         lr, c->cfg.beta1, c->cfg.beta2, c->cfg.adam_eps, c->cfg.weight_decay, c->st));
   }
-  HIPCHK(c, refresh_transposed(c));
   c->armed_step = false;
   c->grads_fresh = true;
   if (h_grad_norm) {
@@ -1075,7 +1001,6 @@ GPT2_API gpt2_status gpt2_sync_weight_copies(gpt2_ctx* c) {
   gpt2_status s = check_ctx(c);
   if (s) return s;
   if (c->h16) HIPCHK(c, gk::to_h16(c->params, c->shadow, c->nflat, c->dt, c->st));
-  HIPCHK(c, refresh_transposed(c));
   return GPT2_OK;
 }
 
@@ -1120,7 +1045,7 @@ GPT2_API gpt2_status gpt2_tensor_info(const gpt2_ctx* c, int32_t i, gpt2_tensor_
 GPT2_API gpt2_status gpt2_timing_enable(gpt2_ctx* c, int32_t kernel_class) {
   gpt2_status s = check_ctx(c);
   if (s) return s;
-  if (kernel_class < 0 || kernel_class > GPT2_T_COLSUM) return fail(c, GPT2_E_ARG, "bad kernel class");
+  if (kernel_class < 0 || kernel_class > GPT2_T_EMBED) return fail(c, GPT2_E_ARG, "bad kernel class");
   c->tclass = kernel_class;
   c->ev_used = 0;
   return GPT2_OK;

@@ -3,14 +3,20 @@
 //   dX       dX = dY W   (B operand transposed in memory)
 //   dW       dW = dY^T X (both operands transposed in memory)
 // 16-bit operands (bf16, or fp16 for the fp16 workload) run on the gfx950
-// matrix cores (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation).
-// Tiles are staged global -> registers -> LDS with a
-// double-buffered LDS ring; operands that are contiguous along M/N instead
-// of K are loaded as 8x8 blocks and transposed in registers (v_perm), so the
-// LDS always holds [row][k] and every MFMA fragment is one 16-byte LDS read.
-// fp32 operands (the all-fp32 configuration) use an LDS-tiled FMA kernel.
+// matrix cores (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation):
+//   * forward and dX: persistent k_gemm_nt, operands loaded straight into an
+//     LDS ring; the dX weight stays [out][in] and its MFMA operands come from
+//     the LDS transpose read;
+//   * dW: persistent k_gemm_tn, both operands [token][feature] in LDS, read
+//     with the LDS transpose, split over tokens when the tiles are few;
+//   * other layouts or alignments: k_gemm_h16, register-staged tiles with
+//     8x8 blocks transposed in registers (v_perm).
+// fp32 operands (the all-fp32 configuration) use the fp32 matrix cores for
+// large problems and an LDS-tiled FMA kernel for small ones.
 // Epilogues fuse bias, tanh-GELU, residual add, the GELU derivative and
 // the weight-gradient accumulation (alpha, beta) into the store.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,6 +38,8 @@ struct GP {
   float alpha, beta;
   int kchunk;  // split-K: K range per split (multiple of the K tile)
   int splits;  // TN kernel: number of K splits (1: write the output directly)
+  float* dbias;     // TN kernel: bias gradient, column sums of A (null: none)
+  float* dbias_ws;  // TN kernel with splits: [splits][M] partial column sums
 };
 
 // ------------------------------------------------------------------ epilogues
@@ -446,6 +454,17 @@ struct BufLoader {
   }
 };
 
+// 16 bytes of row `row` from column k (k % 8 == 0, row 16-byte aligned),
+// zero past column K: the chunk that straddles K is read element by element.
+__device__ __forceinline__ uint4 load_k_chunk(const uint16_t* __restrict__ row, int k, int K) {
+  if (k + 8 <= K) return *(const uint4*)(row + k);
+  uint16_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = k + i < K ? row[k + i] : (uint16_t)0;
+  return make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16, e[4] | (uint32_t)e[5] << 16,
+                    e[6] | (uint32_t)e[7] << 16);
+}
+
 // Ragged last stage (k0 + 32 > K): zero-filled register loads, LDS stores.
 template <int ROWS, int NW>
 __device__ __forceinline__ void issue_tail(const uint16_t* __restrict__ g, long ld, int row0,
@@ -458,10 +477,100 @@ __device__ __forceinline__ void issue_tail(const uint16_t* __restrict__ g, long 
     const int r = blk * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int gr = row0 + r, gk = k0 + c * 8;
-    uint4 v = (gr < nrows && gk < K) ? *(const uint4*)(g + (size_t)gr * ld + gk)
-                                      : make_uint4(0, 0, 0, 0);
+    uint4 v = (gr < nrows && gk < K) ? load_k_chunk(g + (size_t)gr * ld, gk, K) : make_uint4(0, 0, 0, 0);
     *(uint4*)(lds_op + blk * 512 + lane * 8) = v;
   }
+}
+
+// ---------------------------------------------- [k][cols] tiles read with the LDS transpose
+// An operand contiguous along its output dimension (the weight of dX = dY W,
+// both operands of dW = dY^T X) is staged as it lies in memory: 32 k rows of
+// COLS columns, row m's 16-byte chunk p in slot p ^ tok_swz(m).  MFMA
+// operands come from the LDS transpose read (ds_read_b64_tr_b16): a 16-lane
+// group reads a 4 x 16 (k x column) block and lane i receives the 4 k
+// values of column i, so two reads give the 8 k values of a 32x32x16
+// operand.  The two 16-lane groups that share an LDS cycle read 4 rows x 4
+// chunks; the swizzle puts those 16 chunks on distinct 16-byte bank groups:
+// rows 512 or 256 bytes apart (COLS % 128 == 0) start on the same bank and
+// take XOR offsets of 0, 4, 8, 12 chunks; rows 384 bytes apart (COLS = 192)
+// alternate between two bank halves, so rows 2 and 3 of each four take an
+// XOR of 4.  XOR by a multiple of 4 below 8 or 16 keeps the slot in the row.
+constexpr int TK = 32;  // k rows per stage
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+template <int COLS>
+__device__ __forceinline__ int tok_swz(int m) {
+  static_assert(COLS % 64 == 0 && COLS >= 128, "tile width");
+  return COLS % 128 == 0 ? 4 * (m & 3) : 4 * ((m >> 1) & 1);
+}
+
+// Direct-to-LDS stage loads of a [k][COLS] tile.  The descriptor starts at
+// the stage's (k0, c0) and holds the bytes left of the operand's `krows`
+// rows, so rows past the last read as zero (range check of the per-lane
+// offset).  Columns past the operand's width read the next row's data or
+// zero; they feed only output columns that the epilogue drops.
+template <int COLS, int NW>
+struct TokLoader {
+  static constexpr int CPR = COLS / 8;      // 16-byte chunks per k row
+  static constexpr int NI = TK * CPR / 64 / NW;
+  static_assert(NI * 64 * NW == TK * CPR, "tile must split evenly over the waves");
+  void* base;
+  uint32_t nbytes;
+  uint32_t voff[NI];
+  int blk0;
+  __device__ __forceinline__ void init(const void* b, long ld, int krows, int wv, int lane) {
+    uint64_t bytes = (uint64_t)krows * ld * 2;
+    base = const_cast<void*>(b);
+    nbytes = (uint32_t)(bytes > 0xffffffffull ? 0xffffffffull : bytes);
+    blk0 = wv * NI;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int lin = (blk0 + i) * 64 + lane;   // LDS chunk slot
+      const int m = lin / CPR, slot = lin % CPR;
+      const int pch = slot ^ tok_swz<COLS>(m);  // global chunk stored in this slot
+      voff[i] = (uint32_t)((long)m * ld * 2 + pch * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t soff, uint16_t* lds_op) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) buffer_load_lds16(base, nbytes, lds_op + (blk0 + i) * 512, voff[i], soff);
+  }
+};
+
+// Ragged last stage of a [k][COLS] tile (k0 + 32 > K): zero-filled register
+// loads of rows k0.. and columns c0.. (ncols % 8 == 0), LDS stores.
+template <int COLS, int NW>
+__device__ __forceinline__ void tok_tail(const uint16_t* __restrict__ g, long ld, int k0, int K, int c0,
+                                         int ncols, uint16_t* lds_op, int wv, int lane) {
+  constexpr int CPR = COLS / 8, NI = TK * CPR / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int lin = (wv * NI + i) * 64 + lane;
+    const int m = lin / CPR, pch = (lin % CPR) ^ tok_swz<COLS>(m);
+    const int gk = k0 + m, gc = c0 + pch * 8;
+    uint4 v = (gk < K && gc < ncols) ? *(const uint4*)(g + (size_t)gk * ld + gc) : make_uint4(0, 0, 0, 0);
+    *(uint4*)(lds_op + lin * 8) = v;
+  }
+}
+
+// 8 k values (rows ks*16 + 8g .. +7) of column `col` of an LDS tile
+// [32][COLS], as an MFMA operand; lane l serves column cbase + l % 32.
+template <int COLS>
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int cbase, int ks, int lane) {
+  const int G = lane >> 4, q = lane & 15;
+  const int col = cbase + 16 * (G & 1) + 4 * (q & 3);
+  v4s h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int m = ks * 16 + 8 * (G >> 1) + 4 * hh + (q >> 2);
+    const int off = m * COLS + (((col >> 3) ^ tok_swz<COLS>(m)) << 3) + (col & 7);
+    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
+  }
+  return make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
+                    __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]}));
 }
 
 __device__ __forceinline__ int tile_pid(int round, int G) {
@@ -480,14 +589,19 @@ __device__ __forceinline__ void grouped_coords(int pid, int nm, int nn, int& tm,
   tn = in / gsz;
 }
 
-template <typename TE, int BM, int BN, int WM, int WN, int EPI>
+// BKN: B is stored [K][N] (the weight of dX = dY W) and staged as a [k][BN]
+// tile read with the LDS transpose (TokLoader / tr_frag); otherwise B is
+// [N][K] like A.
+template <typename TE, int BM, int BN, int WM, int WN, int EPI, bool BKN>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   typedef typename H16<TE>::v8 v8;
+  typedef typename std::conditional<BKN, TokLoader<BN, WM * WN>, BufLoader<BN, WM * WN>>::type LoaderB;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(NK == TK, "A and B stages cover the same k");
   constexpr int STAGE = (BM + BN) * NK;  // 16-bit elements per stage
-  constexpr int PER = BufLoader<BM, NW>::NI + BufLoader<BN, NW>::NI;  // loads per stage
+  constexpr int PER = BufLoader<BM, NW>::NI + LoaderB::NI;  // loads per stage
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -504,9 +618,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   const bool ragged = (p.K % NK) != 0;
 
   BufLoader<BM, NW> la;
-  BufLoader<BN, NW> lb;
+  LoaderB lb;
   la.init(p.A, p.lda, p.M, wv, lane);
-  lb.init(p.B, p.ldb, p.N, wv, lane);
+  lb.init(p.B, p.ldb, BKN ? p.K : p.N, wv, lane);
 
   // issue-side cursor: stage t = (round, kt)
   int i_round = 0, i_kt = 0, i_tm = 0, i_tn = 0;
@@ -516,10 +630,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
     const int k0 = i_kt * NK;
     if (ragged && k0 + NK > p.K) {
       issue_tail<BM, NW>((const uint16_t*)p.A, p.lda, i_tm * BM, p.M, k0, p.K, st, wv, lane);
-      issue_tail<BN, NW>((const uint16_t*)p.B, p.ldb, i_tn * BN, p.N, k0, p.K, st + BM * NK, wv, lane);
+      if constexpr (BKN)
+        tok_tail<BN, NW>((const uint16_t*)p.B, p.ldb, k0, p.K, i_tn * BN, p.N, st + BM * NK, wv, lane);
+      else
+        issue_tail<BN, NW>((const uint16_t*)p.B, p.ldb, i_tn * BN, p.N, k0, p.K, st + BM * NK, wv, lane);
     } else {
       la.issue((uint32_t)(((long)i_tm * BM * p.lda + k0) * 2), st);
-      lb.issue((uint32_t)(((long)i_tn * BN * p.ldb + k0) * 2), st + BM * NK);
+      if constexpr (BKN)
+        lb.issue((uint32_t)(((long)k0 * p.ldb + i_tn * BN) * 2), st + BM * NK);
+      else
+        lb.issue((uint32_t)(((long)i_tn * BN * p.ldb + k0) * 2), st + BM * NK);
     }
     if (++i_kt == nk) {
       i_kt = 0;
@@ -554,8 +674,12 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
     for (int i = 0; i < FM; ++i)
       af[set][i] = __builtin_bit_cast(v8, *(const uint4*)(As + ((wm + i * 32 + fr) * 4 + slot) * 8));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[set][j] = __builtin_bit_cast(v8, *(const uint4*)(Bs + ((wn + j * 32 + fr) * 4 + slot) * 8));
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (BKN)
+        bfr[set][j] = __builtin_bit_cast(v8, tr_frag<BN>(Bs, wn + j * 32, ks, lane));
+      else
+        bfr[set][j] = __builtin_bit_cast(v8, *(const uint4*)(Bs + ((wn + j * 32 + fr) * 4 + slot) * 8));
+    }
   };
   auto mfma_set = [&](int set) {
 #pragma unroll
@@ -625,67 +749,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
 
 // ------------------------------------------------------------------ 16-bit TN kernel (weight gradients)
 // D[r][c] = sum_m A[m * lda + r] * B[m * ldb + c]: both operands keep their
-// natural [token][feature] layout.  Stages of 32 tokens are loaded straight
-// into LDS (buffer loads whose descriptor starts at the stage's first token,
-// so tokens past the last one fail the range check of the per-lane offset
-// and read as zero: a ragged token count needs no special path) as
-// [m][cols] tiles whose 16-byte chunk p of
-// row m sits at p ^ 4 (m % 4); MFMA operands are built with the LDS
-// transpose read (ds_read_b64_tr_b16): each 16-lane group reads a 4 x 16
-// (token x feature) block and lane i receives the 4 tokens of feature i, so
-// two reads give the 8 k values of a 32x32x16 operand.  The swizzle keeps
-// the two 16-lane groups that share a cycle on all 64 banks.
-constexpr int TK = 32;  // tokens per stage
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-
-template <int COLS, int NW>
-struct TokLoader {
-  static constexpr int CPR = COLS / 8;      // 16-byte chunks per token row
-  static constexpr int NI = TK * CPR / 64 / NW;
-  static_assert(CPR >= 16 && NI * 64 * NW == TK * CPR, "tile width must be >= 128, split evenly");
-  void* base;
-  uint32_t nbytes;
-  uint32_t voff[NI];
-  int blk0;
-  __device__ __forceinline__ void init(const void* b, long ld, int M, int wv, int lane) {
-    uint64_t bytes = (uint64_t)M * ld * 2;
-    base = const_cast<void*>(b);
-    nbytes = (uint32_t)(bytes > 0xffffffffull ? 0xffffffffull : bytes);
-    blk0 = wv * NI;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int lin = (blk0 + i) * 64 + lane;   // LDS chunk slot
-      const int m = lin / CPR, slot = lin % CPR;
-      const int pch = slot ^ (4 * (m & 3));     // global chunk stored in this slot
-      voff[i] = (uint32_t)((long)m * ld * 2 + pch * 16);
-    }
-  }
-  __device__ __forceinline__ void issue(uint32_t soff, uint16_t* lds_op) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) buffer_load_lds16(base, nbytes, lds_op + (blk0 + i) * 512, voff[i], soff);
-  }
-};
-
-// 8 k values (tokens ks*16 + 8g .. +7) of feature column `col` of an LDS tile
-// [32][COLS], as an MFMA operand; lane l serves column base + l % 32.
-template <int COLS>
-__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int cbase, int ks, int lane) {
-  const int G = lane >> 4, q = lane & 15;
-  const int col = cbase + 16 * (G & 1) + 4 * (q & 3);
-  v4s h[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int m = ks * 16 + 8 * (G >> 1) + 4 * hh + (q >> 2);
-    const int off = m * COLS + (((col >> 3) ^ (4 * (m & 3))) << 3) + (col & 7);
-    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
-  }
-  return make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
-                    __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
-                    __builtin_bit_cast(uint32_t, (short2){h[1][0], h[1][1]}),
-                    __builtin_bit_cast(uint32_t, (short2){h[1][2], h[1][3]}));
-}
-
+// natural [token][feature] layout and are staged as [k][cols] tiles of 32
+// tokens.  A ragged token count needs no special path: tokens past the last
+// one fail the range check of the per-lane offset and read as zero.
 template <typename TE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
   typedef typename H16<TE>::v8 v8;
@@ -777,6 +843,23 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = H16<TE>::mfma(bfr[set][j], af[set][i], acc[i][j]);
   };
+  // Bias gradient: column sums of A over the tokens.  Lane l's A fragment
+  // holds 8 tokens of row wm + i*32 + l % 32, so the waves of the first
+  // column tile with wn == 0 (one per row block) add up the fragments they
+  // already hold; lanes l and l + 32 hold the two token halves.
+  float bsum[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) bsum[i] = 0.f;
+  auto add_sums = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint4 u = __builtin_bit_cast(uint4, af[set][i]);
+      float v = H16<TE>::add_pair(u.x, bsum[i]);
+      v = H16<TE>::add_pair(u.y, v);
+      v = H16<TE>::add_pair(u.z, v);
+      bsum[i] = H16<TE>::add_pair(u.w, v);
+    }
+  };
 
   if (total > 0) {
     const int pro = min(NS - 1, total);
@@ -790,16 +873,36 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
     int tm, tn, z;
     set_item(round, tm, tn, z);
     const int nk = item_nk(z);
+    const bool sums = p.dbias != nullptr && tn == 0 && wn == 0;  // uniform per wave
     for (int kt = 0; kt < nk; ++kt, ++s) {
       if (s + NS - 1 < total) issue_next(s + NS - 1);
       load_frags(s, 1, 1);
       mfma_set(0);
+      if (sums) add_sums(0);
       if (s + 1 < total) load_frags(s + 1, 0, 0);
       if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
       stage_barrier();
       mfma_set(1);
+      if (sums) add_sums(1);
     }
     const int m0 = tm * BM, n0 = tn * BN;
+    if (sums) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float v = bsum[i] + __shfl_xor(bsum[i], 32, 64);
+        bsum[i] = 0.f;
+        const int r = m0 + wm + i * 32 + fr;
+        if (g == 0 && r < p.M) {
+          if (S > 1) {
+            p.dbias_ws[(size_t)z * p.M + r] = v;
+          } else {
+            float o = p.alpha * v;
+            if (p.beta != 0.f) o += p.beta * p.dbias[r];
+            p.dbias[r] = o;
+          }
+        }
+      }
+    }
     float* op = (float*)p.out + (S > 1 ? (size_t)z * p.M * p.ldo : 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -1003,10 +1106,22 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(GP p) {
 }
 
 // ------------------------------------------------------------------ split-K reduction
+// out = alpha * sum_z ws[z][0..n) + beta * out, and likewise out2 from the
+// [S][n2] partials ws2 (the TN kernel's bias-gradient sums; n2 may be 0),
+// the splits added in order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int S,
-                                                       size_t n, float* out, float alpha,
-                                                       float beta) {
+                                                       size_t n, float* out,
+                                                       const float* __restrict__ ws2, size_t n2,
+                                                       float* out2, float alpha, float beta) {
   const size_t n4 = n / 4;  // n is a multiple of 4 (N % 4 == 0 when split)
+  for (size_t j = n4 + (size_t)blockIdx.x * 256 + threadIdx.x; j < n4 + n2; j += (size_t)gridDim.x * 256) {
+    const size_t i = j - n4;
+    float sum = 0.f;
+    for (int z = 0; z < S; ++z) sum += ws2[(size_t)z * n2 + i];
+    float r = alpha * sum;
+    if (beta != 0.f) r += beta * out2[i];
+    out2[i] = r;
+  }
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
     // the partials are added in split order; loads go out 8 at a time so
     // their latencies overlap instead of adding up
@@ -1079,7 +1194,8 @@ static Plan plan_gemm(int M, int N, int K, bool wgrad, size_t ws_elems) {
 struct TnPlan {
   int cfg, splits, kchunk;
 };
-static TnPlan plan_tn(int M, int N, int K, size_t ws_elems) {
+// extra: workspace floats per split beyond the M x N partial (bias sums).
+static TnPlan plan_tn(int M, int N, int K, size_t ws_elems, size_t extra) {
   const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128}, per_cu[3] = {1, 1, 2};
   const double eff[3] = {1.0, 0.65, 0.55};
   const double cu_flops = 2.5e15 / 256.0, hbm = 6.0e12;
@@ -1090,7 +1206,7 @@ static TnPlan plan_tn(int M, int N, int K, size_t ws_elems) {
     for (int S = 1; S <= 32; ++S) {
       int kchunk = cdiv(cdiv(K, S), TK) * TK;
       if (cdiv(K, kchunk) != S) continue;
-      if (S > 1 && (size_t)S * M * N > ws_elems) continue;
+      if (S > 1 && (size_t)S * ((size_t)M * N + extra) > ws_elems) continue;
       long slots = 256L * per_cu[c];
       long waves = (tiles * S + slots - 1) / slots;
       double t = waves * per_cu[c] * (2.0 * bm[c] * bn[c] * kchunk) / (cu_flops * eff[c]);
@@ -1107,8 +1223,8 @@ static TnPlan plan_tn(int M, int N, int K, size_t ws_elems) {
 size_t gemm_splitk_ws_elems(int M, int N, int K) {
   Plan pl = plan_gemm(M, N, K, true, (size_t)-1);
   size_t a = pl.splits > 1 ? (size_t)pl.splits * M * N : 0;
-  TnPlan tp = plan_tn(M, N, K, (size_t)-1);
-  size_t b = tp.splits > 1 ? (size_t)tp.splits * M * N : 0;
+  TnPlan tp = plan_tn(M, N, K, (size_t)-1, M);
+  size_t b = tp.splits > 1 ? (size_t)tp.splits * ((size_t)M * N + M) : 0;
   return a > b ? a : b;
 }
 
@@ -1145,22 +1261,33 @@ static int plan_nt(int M, int N) {
   return best;
 }
 
-template <typename TE, int BM, int BN, int WM, int WN, int EPI>
+template <typename TE, int BM, int BN, int WM, int WN, int EPI, bool BKN>
 static void launch_nt(GP q, hipStream_t st) {
   int tiles = cdiv(q.M, BM) * cdiv(q.N, BN);
   int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
-  k_gemm_nt<TE, BM, BN, WM, WN, EPI><<<grid, WM * WN * 64, 0, st>>>(q);
+  k_gemm_nt<TE, BM, BN, WM, WN, EPI, BKN><<<grid, WM * WN * 64, 0, st>>>(q);
+}
+
+// The weight-gradient shapes the TN kernel takes (it also forms the bias
+// gradient, when asked, from the A fragments it holds).
+static bool tn_direct(const GemmArgs& a) {
+  return (a.dt == ACT_BF16 || a.dt == ACT_F16) && a.kind == EPI_WGRAD && a.a_t && a.b_t && a.N % 4 == 0 &&
+         a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws;
 }
 
 template <typename TE, bool AT, bool BT, int EPI>
 static hipError_t launch_h16(const GemmArgs& a, GP p, hipStream_t st) {
   if constexpr (AT && BT && EPI == EPI_WGRAD) {
-    if (a.N % 4 == 0 && a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws) {
-      TnPlan tp = plan_tn(a.M, a.N, a.K, a.splitk_ws_elems);
+    if (tn_direct(a)) {
+      TnPlan tp = plan_tn(a.M, a.N, a.K, a.splitk_ws_elems, a.dbias ? a.M : 0);
       p.kchunk = tp.kchunk;
       p.splits = tp.splits;
       GP q = p;
-      if (tp.splits > 1) q.out = a.splitk_ws;
+      q.dbias = a.dbias;
+      if (tp.splits > 1) {
+        q.out = a.splitk_ws;
+        if (a.dbias) q.dbias_ws = a.splitk_ws + (size_t)tp.splits * a.M * a.N;
+      }
       switch (tp.cfg) {
         case 0: launch_tn<TE, 256, 256, 4, 2>(q, 1, st); break;
         case 1: launch_tn<TE, 256, 128, 2, 2>(q, 1, st); break;
@@ -1168,18 +1295,21 @@ static hipError_t launch_h16(const GemmArgs& a, GP p, hipStream_t st) {
       }
       if (tp.splits > 1) {
         size_t n = (size_t)a.M * a.N;
-        k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, tp.splits, n, (float*)a.out, a.alpha, a.beta);
+        k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, tp.splits, n, (float*)a.out, q.dbias_ws,
+                                              a.dbias ? (size_t)a.M : 0, a.dbias, a.alpha, a.beta);
       }
       return hipGetLastError();
     }
   }
-  if constexpr (!AT && !BT && EPI != EPI_WGRAD) {
-    if (a.K % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0) {
+  // Forward (B = [N][K]) and dX (B = [K][N], N % 8 == 0): any K, the last
+  // partial stage zero-filled.
+  if constexpr (!AT && EPI != EPI_WGRAD) {
+    if (a.lda % 8 == 0 && a.ldb % 8 == 0 && (!BT || a.N % 8 == 0)) {
       p.kchunk = a.K;
       switch (plan_nt(a.M, a.N)) {
-        case 0: launch_nt<TE, 256, 256, 4, 2, EPI>(p, st); break;
-        case 1: launch_nt<TE, 256, 192, 2, 2, EPI>(p, st); break;
-        default: launch_nt<TE, 256, 128, 2, 2, EPI>(p, st); break;
+        case 0: launch_nt<TE, 256, 256, 4, 2, EPI, BT>(p, st); break;
+        case 1: launch_nt<TE, 256, 192, 2, 2, EPI, BT>(p, st); break;
+        default: launch_nt<TE, 256, 128, 2, 2, EPI, BT>(p, st); break;
       }
       return hipGetLastError();
     }
@@ -1197,7 +1327,8 @@ static hipError_t launch_h16(const GemmArgs& a, GP p, hipStream_t st) {
   }
   if (pl.splits > 1) {
     size_t n = (size_t)a.M * a.N;
-    k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, pl.splits, n, (float*)a.out, a.alpha, a.beta);
+    k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, pl.splits, n, (float*)a.out, nullptr, 0, nullptr,
+                                          a.alpha, a.beta);
   }
   return hipGetLastError();
 }
@@ -1221,7 +1352,8 @@ static hipError_t launch_f32(const GemmArgs& a, GP p, hipStream_t st) {
     if (S > 1) q.out = a.splitk_ws;
     k_gemm_f32m<AT, BT, EPI><<<dim3(cdiv(a.N, F32M_BM), cdiv(a.M, F32M_BM), S), 256, 0, st>>>(q);
     if (S > 1)
-      k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, S, (size_t)a.M * a.N, (float*)a.out, a.alpha, a.beta);
+      k_splitk_reduce<<<2048, 256, 0, st>>>(a.splitk_ws, S, (size_t)a.M * a.N, (float*)a.out, nullptr, 0,
+                                            nullptr, a.alpha, a.beta);
     return hipGetLastError();
   }
   p.kchunk = a.K;
@@ -1267,20 +1399,27 @@ static hipError_t dispatch_t(const GemmArgs& a, const GP& p, hipStream_t st) {
 
 hipError_t gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.dbias && (a.kind != EPI_WGRAD || !a.a_t || a.alpha != 1.f)) return hipErrorInvalidValue;
+  const bool bias_apart = a.dbias && !tn_direct(a);
+  if (bias_apart && !a.colsum_ws) return hipErrorInvalidValue;
   GP p;
   p.M = a.M; p.N = a.N; p.K = a.K;
   p.A = a.A; p.lda = a.lda; p.B = a.B; p.ldb = a.ldb;
   p.out = a.out; p.ldo = a.ldo; p.out2 = a.out2; p.aux = a.aux; p.bias = a.bias;
   p.alpha = a.alpha; p.beta = a.beta; p.kchunk = a.K; p.splits = 1;
+  p.dbias = nullptr; p.dbias_ws = nullptr;
+  hipError_t e = hipErrorInvalidValue;
   switch (a.kind) {
-    case EPI_STORE: return dispatch_t<EPI_STORE>(a, p, st);
-    case EPI_LOGITS: return dispatch_t<EPI_LOGITS>(a, p, st);
-    case EPI_GELU: return dispatch_t<EPI_GELU>(a, p, st);
-    case EPI_RESID: return dispatch_t<EPI_RESID>(a, p, st);
-    case EPI_DGELU: return dispatch_t<EPI_DGELU>(a, p, st);
-    case EPI_WGRAD: return dispatch_t<EPI_WGRAD>(a, p, st);
+    case EPI_STORE: e = dispatch_t<EPI_STORE>(a, p, st); break;
+    case EPI_LOGITS: e = dispatch_t<EPI_LOGITS>(a, p, st); break;
+    case EPI_GELU: e = dispatch_t<EPI_GELU>(a, p, st); break;
+    case EPI_RESID: e = dispatch_t<EPI_RESID>(a, p, st); break;
+    case EPI_DGELU: e = dispatch_t<EPI_DGELU>(a, p, st); break;
+    case EPI_WGRAD: e = dispatch_t<EPI_WGRAD>(a, p, st); break;
   }
-  return hipErrorInvalidValue;
+  // A ([K tokens][M features]) column sums where the GEMM kernel did not form them
+  if (e == hipSuccess && bias_apart) e = colsum(a.A, a.dt, a.K, a.M, a.lda, a.dbias, a.beta, a.colsum_ws, st);
+  return e;
 }
 
 }  // namespace gk

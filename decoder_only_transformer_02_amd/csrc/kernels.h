@@ -67,16 +67,6 @@ struct AdamChunk {
 hipError_t adamw(float* p, const float* g, float* m, float* v, uint16_t* shadow, int shadow_dt,
                  const AdamChunk* chunks, int nchunks, const float* scal, float lr, float beta1,
                  float beta2, float eps, float wd, hipStream_t st);
-// Transposes of several 16-bit matrices in one launch: job j does
-// dst_base[dst + c * ldt + r] = src_base[src + r * C + c] (ldt even, element
-// offsets) over the 64 x 64 tiles [first_tile, first_tile + ceil(R/64)
-// ceil(C/64)); jobs ordered by first_tile, total_tiles the sum.
-struct TransposeJob {
-  uint64_t src, dst;
-  int32_t R, C, ldt, first_tile;
-};
-hipError_t transpose_jobs(const uint16_t* src_base, uint16_t* dst_base, const TransposeJob* jobs, int njobs,
-                          int total_tiles, hipStream_t st);
 // 16-bit copy (bf16 or fp16 per dt, round to nearest even) of n fp32 values.
 hipError_t to_h16(const float* x, uint16_t* y, size_t n, int dt, hipStream_t st);
 hipError_t fill_f32(float* x, size_t n, float v, hipStream_t st);
@@ -109,9 +99,16 @@ struct GemmArgs {
   int dt;                // operand / activation storage type (ActType)
   float* splitk_ws;      // EPI_WGRAD split-K partials (may be null -> no split)
   size_t splitk_ws_elems;
+  // EPI_WGRAD only, alpha == 1: also dbias[r] = beta dbias[r] + sum_k A[k][r]
+  // (the bias gradient: column sums of dY).  The TN kernel forms it from
+  // the A fragments it holds; other paths run colsum on A with colsum_ws
+  // (colsum_part_floats(K, M) floats).  Null: no bias gradient.
+  float* dbias = nullptr;
+  float* colsum_ws = nullptr;
 };
 hipError_t gemm(const GemmArgs& a, hipStream_t st);
-// Workspace floats that EPI_WGRAD may use for split-K at this size.
+// Workspace floats that EPI_WGRAD may use for split-K at this size (the
+// bias-gradient partials included).
 size_t gemm_splitk_ws_elems(int M, int N, int K);
 
 // ---------------------------------------------------------------- attention

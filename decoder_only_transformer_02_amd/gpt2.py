@@ -22,8 +22,7 @@ STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_STATE", -4: "E_HIP", -5: "
 GPT2_FP32, GPT2_BF16, GPT2_FP16 = 0, 1, 2
 KINDS = ["param", "grad", "adam_m", "adam_v", "shadow", "act", "logits", "scalar"]
 TIMING = {"none": 0, "lmhead_fwd": 1, "gemm": 2, "attn_fwd": 3, "attn_bwd": 4, "ln_fwd": 5,
-          "ln_bwd": 6, "xent": 7, "adamw": 8, "norm": 9, "transpose": 10, "embed": 11,
-          "colsum": 12}
+          "ln_bwd": 6, "xent": 7, "adamw": 8, "norm": 9, "embed": 10}
 
 # every symbol declared in include/gpt2.h
 EXPORTS = ["gpt2_default_config", "gpt2_arena_bytes", "gpt2_num_params", "gpt2_init_host",

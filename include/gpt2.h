@@ -237,7 +237,7 @@ gpt2_status gpt2_block_fwd_bwd(gpt2_ctx* c, int32_t layer, const float* d_x, con
  * moments (tensor kinds GPT2_K_PARAM, GPT2_K_ADAM_M, GPT2_K_ADAM_V, read and
  * written through the tensor table's views) and the optimizer step count.
  * After writing parameters into a context, gpt2_sync_weight_copies rewrites
- * the bf16 copies (and their transposed copies) that the GEMMs read from the
+ * the 16-bit weight copies that the GEMMs read from the
  * fp32 parameters; a context resumed this way continues bitwise like the
  * one that was saved.  The step count t (AdamW's bias corrections use t + 1
  * at the next step) lives on the device: get synchronizes the stream and
@@ -266,14 +266,13 @@ gpt2_status gpt2_tensor_info(const gpt2_ctx* c, int32_t i, gpt2_tensor_desc* out
  * reduction, ...).  Classes: the classifier forward GEMM alone; every GEMM
  * (the classifier forward included); attention forward; attention backward;
  * LayerNorm forward; LayerNorm backward; cross-entropy; AdamW; gradient
- * norm; refresh of the transposed bf16 weight copies; embedding forward and
- * backward; bias-gradient column sums.  gpt2_timing_read synchronizes,
- * returns the summed milliseconds and the bracket count since the last
- * read, and resets them. */
+ * norm; embedding forward and backward.  The bias gradients are formed
+ * inside the weight-gradient GEMMs and time with the GEMM class.
+ * gpt2_timing_read synchronizes, returns the summed milliseconds and the
+ * bracket count since the last read, and resets them. */
 enum { GPT2_T_NONE = 0, GPT2_T_LMHEAD_FWD = 1, GPT2_T_GEMM = 2, GPT2_T_ATTN_FWD = 3,
        GPT2_T_ATTN_BWD = 4, GPT2_T_LN_FWD = 5, GPT2_T_LN_BWD = 6, GPT2_T_XENT = 7,
-       GPT2_T_ADAMW = 8, GPT2_T_NORM = 9, GPT2_T_TRANSPOSE = 10, GPT2_T_EMBED = 11,
-       GPT2_T_COLSUM = 12 };
+       GPT2_T_ADAMW = 8, GPT2_T_NORM = 9, GPT2_T_EMBED = 10 };
 gpt2_status gpt2_timing_enable(gpt2_ctx* c, int32_t kernel_class);
 gpt2_status gpt2_timing_read(gpt2_ctx* c, double* total_ms, int64_t* launches);
 

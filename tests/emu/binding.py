@@ -30,6 +30,7 @@ def emu_lib():
             "emu_set_land_early": (None, [I]),
             "emu_collectives": (ct.c_long, []),
             "emu_gemm": (I, [I, I, I, P, I, I, P, I, I, I, P, I, P, P, P, F, F, I, P, SZ]),
+            "emu_gemm_wgrad_bias": (I, [I, I, I, P, I, P, I, P, I, F, F, I, P, SZ, P, P]),
             "emu_gemm_splitk_ws_elems": (SZ, [I, I, I]),
             "emu_attn_fwd": (I, [P, P, P, I, I, I, I, I]),
             "emu_attn_bwd_ws": (SZ, [I, I, I]),
@@ -42,7 +43,6 @@ def emu_lib():
             "emu_ln_bwd": (I, [P, P, P, P, P, I, P, P, I, P, I, I, P, P, F]),
             "emu_colsum_part_floats": (SZ, [I, I]),
             "emu_colsum": (I, [P, I, I, I, I, P, F, P]),
-            "emu_transpose_jobs": (I, [P, P, P, I, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)

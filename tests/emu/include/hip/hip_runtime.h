@@ -271,6 +271,10 @@ inline void __syncthreads() { ::emu::syncthreads(); }
 #define __builtin_amdgcn_perm(a, b, s) ::emu::perm(a, b, s)
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
 #define __builtin_amdgcn_rcpf(x) (1.0f / (x))
+// a.lo * b.lo + a.hi * b.hi + c (two-element dot products into fp32)
+#define __builtin_amdgcn_fdot2_f32_bf16(a, b, c, clamp) \
+  ((float)(a)[0] * (float)(b)[0] + (float)(a)[1] * (float)(b)[1] + (c))
+#define __builtin_amdgcn_fdot2(a, b, c, clamp) ((float)(a)[0] * (float)(b)[0] + (float)(a)[1] * (float)(b)[1] + (c))
 
 template <typename T>
 inline T __shfl_xor(T v, int mask, int width = 64) { return ::emu::shfl_xor<T>(v, mask, width); }

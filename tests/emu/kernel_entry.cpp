@@ -21,6 +21,22 @@ EMU_API int emu_gemm(int M, int N, int K, const void* A, int lda, int a_t, const
   return (int)gk::gemm(a, nullptr);
 }
 
+// Weight gradient out = alpha A^T B + beta out (A [K][M], B [K][N]) with the
+// bias gradient dbias = beta dbias + sum_k A[k][:] (alpha must be 1 then).
+EMU_API int emu_gemm_wgrad_bias(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* out,
+                                int ldo, float alpha, float beta, int dt, float* ws, size_t ws_elems,
+                                float* dbias, float* colsum_ws) {
+  gk::GemmArgs a;
+  a.M = M; a.N = N; a.K = K;
+  a.A = A; a.lda = lda; a.a_t = true;
+  a.B = B; a.ldb = ldb; a.b_t = true;
+  a.kind = gk::EPI_WGRAD; a.out = out; a.ldo = ldo; a.out2 = nullptr; a.aux = nullptr; a.bias = nullptr;
+  a.alpha = alpha; a.beta = beta; a.dt = dt;
+  a.splitk_ws = ws; a.splitk_ws_elems = ws_elems;
+  a.dbias = dbias; a.colsum_ws = colsum_ws;
+  return (int)gk::gemm(a, nullptr);
+}
+
 EMU_API size_t emu_gemm_splitk_ws_elems(int M, int N, int K) { return gk::gemm_splitk_ws_elems(M, N, K); }
 
 EMU_API int emu_attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int dt) {
@@ -67,8 +83,3 @@ EMU_API int emu_colsum(const void* X, int dt, int M, int N, int ldx, float* db, 
   return (int)gk::colsum(X, dt, M, N, ldx, db, beta, part, nullptr);
 }
 
-// jobs: njobs x {src, dst (element offsets), R, C, ldt, first_tile} packed as
-// the library's TransposeJob.
-EMU_API int emu_transpose_jobs(const uint16_t* src, uint16_t* dst, const void* jobs, int njobs, int tiles) {
-  return (int)gk::transpose_jobs(src, dst, (const gk::TransposeJob*)jobs, njobs, tiles, nullptr);
-}

@@ -37,8 +37,7 @@ def test_class_work_matches_the_scope_table_figures():
     GEMMs 3 x 2.783 TF (layers) + 3 x 1.266 TF (classifier); attention
     0.3095 TF forward, twice that backward; LayerNorm (6C+8) and (14C+8)
     bytes per token over 25 LayerNorms; cross-entropy (4 Vp + 8) bytes per
-    token; norm 4 and AdamW 30 bytes per parameter; 4 bytes per GEMM-weight
-    element for the transposed copies."""
+    token; norm 4 and AdamW 30 bytes per parameter."""
     p = PRESETS["gpt2_124m"]
     w = bench.class_work(p, 16, 1024, 124_475_904)
     assert w["gemm"][1] == 3 * 2 * 16384 * (12 * 12 * 768 * 768 + 50304 * 768)
@@ -51,10 +50,9 @@ def test_class_work_matches_the_scope_table_figures():
     assert abs(w["xent"][1] / 1e9 - 3.30) < 0.01
     assert abs(w["norm"][1] / 1e9 - 0.498) < 0.001
     assert abs(w["adamw"][1] / 1e9 - 3.734) < 0.001
-    assert w["transpose"][1] == 4 * (50304 * 768 + 12 * 4 * 3 * 768 * 768)  # qkv 3CC, proj CC, fc 4CC, mproj 4CC
     assert {k: v[0] for k, v in w.items()} == {
         "lmhead_fwd": "mfma", "gemm": "mfma", "attn_fwd": "mfma", "attn_bwd": "mfma", "ln_fwd": "hbm",
-        "ln_bwd": "hbm", "xent": "hbm", "norm": "hbm", "adamw": "hbm", "transpose": "hbm"}
+        "ln_bwd": "hbm", "xent": "hbm", "norm": "hbm", "adamw": "hbm"}
 
 
 def test_roofline_entry_and_percentiles():
@@ -113,9 +111,9 @@ def test_bench_control_flow_on_the_emulated_library(monkeypatch, capsys):
     assert rec["metric"] == bench.METRIC and rec["steps"] == 3 and rec["n_gpus"] == 1
     assert rec["roofline"]["bound"] == "mfma" and rec["roofline"]["launches"] == 1
     assert set(rec["kernels"]) >= {"gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "xent", "adamw",
-                                   "norm", "transpose", "embed", "colsum"}
+                                   "norm", "embed"}
     assert rec["kernels"]["attn_fwd"]["launches_per_step"] == small["n_layer"]
-    assert rec["kernels"]["transpose"]["launches_per_step"] == 1
+    assert "transpose" not in rec["kernels"] and "colsum" not in rec["kernels"]
     assert rec["kernels"]["ln_fwd"]["launches_per_step"] == 2 * small["n_layer"] + 1
     assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
     assert rec["accumulated_step"]["tokens_per_step"] == 2 * 16 * 2

@@ -4,14 +4,18 @@ matrix product, a scatter-add, the oracle's LayerNorm, attention and
 cross-entropy).  The whole step cannot be emulated at these sizes in a CPU
 suite, but each family can, with the tile configuration and split-K plan of
 the real launch:
-  * forward/dX GEMMs at M = 16384 rows (the 256x192 and 256x256 tiles) with
+  * forward GEMMs at M = 16384 rows (the 256x192 and 256x256 tiles) with
     every epilogue, and the zero-filled ragged K stage;
+  * dX GEMMs reading the weight in place ([K][N]) on the same tiles, with
+    ragged k stages, K not a multiple of 8, ragged rows and columns;
   * weight-gradient GEMMs at K = 16384 tokens (256x128 tiles, 14 K splits)
     and a 256x256 split plan with a ragged token tail, under both buffer
     range-check modes;
   * the embedding backward's sort and segmented sums over 16384 Zipf ids;
   * cross-entropy rows of 50304 and 50257 logits;
-  * LayerNorm forward/backward over 16384 rows; bias-gradient column sums;
+  * bias gradients formed inside the weight-gradient GEMM (split and
+    unsplit plans) or by the column-sum kernel where that GEMM cannot;
+  * LayerNorm forward/backward over 16384 rows; column sums;
   * flash attention forward/backward at T = 1024.
 Larger real shapes run when the environment sets EMU_124M=1."""
 import os
@@ -98,6 +102,33 @@ def test_emu_nt_gemm_full_rows(L, N, K, epi):
         close(f64(out), acc * O.gelu_tanh_grad(f64(aux)), 2 ** -8, "gelu derivative")
 
 
+@pytest.mark.parametrize("M,N,K,lda,epi", [
+    (16384, 768, 96, 96, EPI_STORE),     # 256x192 tiles: the dX shapes with C outputs
+    (16384, 3072, 64, 64, EPI_DGELU),    # 256x256 tiles: mproj dX with gelu'
+    (16384, 768, 72, 72, EPI_STORE),     # ragged last k stage, zero-filled
+    (300, 128, 1001, 1008, EPI_STORE),   # 256x128 tiles, ragged rows, K % 8 != 0 (unpadded vocabulary)
+    (300, 200, 1000, 1000, EPI_DGELU),   # ragged output columns inside the last tile
+])
+def test_emu_nn_gemm_weight_read_in_place(L, M, N, K, lda, epi):
+    """dX = dY W with W stored [K][N] (the weight's own [out][in] layout):
+    B staged as [k][cols] tiles and read with the LDS transpose."""
+    rng = np.random.default_rng(M + N + K + epi)
+    A = bf16(rng.standard_normal((M, lda)))
+    A[:, K:] = float("nan")   # columns past K must not be read
+    W = bf16(rng.standard_normal((K, N)) * 0.1)
+    aux = bf16(rng.standard_normal((M, N))) if epi == EPI_DGELU else None
+    out = torch.zeros((M, N), dtype=torch.bfloat16)
+    alpha = 0.5 if epi == EPI_STORE else 1.0
+    st = L.emu_gemm(M, N, K, ptr(A), lda, 0, ptr(W), N, 1, epi, ptr(out), N, None,
+                    ptr(aux) if aux is not None else None, None, alpha, 0.0, 1, None, 0)
+    assert st == 0
+    acc = f64(A[:, :K]) @ f64(W)
+    if epi == EPI_STORE:
+        close(f64(out), alpha * acc, 2 ** -8, "store")
+    else:
+        close(f64(out), acc * O.gelu_tanh_grad(f64(aux)), 2 ** -8, "gelu derivative")
+
+
 # ---------------------------------------------------------------------------- weight-gradient GEMMs
 
 def _tn(L, M, N, K, alpha, beta, seed):
@@ -126,6 +157,54 @@ def test_emu_tn_gemm(L, range_mode, M, N, K, alpha, beta):
     L.emu_set_range_mode(range_mode)
     got, ref = _tn(L, M, N, K, alpha, beta, M + N + K)
     close(got, ref, 1e-5, f"TN {M}x{N}x{K}")
+
+
+def _wgrad_bias(L, M, N, K, beta, dt, with_ws=True, seed=0):
+    """dW = A^T B + beta dW and db = beta db + column sums of A, through the
+    library's GEMM entry with a bias gradient requested."""
+    rng = np.random.default_rng(seed)
+    tt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dt]
+    A = torch.from_numpy(rng.standard_normal((K, M)).astype(np.float32)).to(tt)
+    B = torch.from_numpy(rng.standard_normal((K, N)).astype(np.float32)).to(tt)
+    out0 = rng.standard_normal((M, N)).astype(np.float32)
+    db0 = rng.standard_normal(M).astype(np.float32)
+    out = torch.from_numpy(out0.copy())
+    db = db0.copy()
+    ws_n = L.emu_gemm_splitk_ws_elems(M, N, K) if with_ws else 0
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.float32)
+    cs = np.zeros(L.emu_colsum_part_floats(K, M), np.float32)
+    st = L.emu_gemm_wgrad_bias(M, N, K, ptr(A), M, ptr(B), N, ptr(out), N, 1.0, beta, dt,
+                               ptr(ws) if with_ws else None, ws_n, ptr(db), ptr(cs))
+    assert st == 0
+    a = A.double().numpy()
+    ref = a.T @ B.double().numpy() + beta * out0.astype(np.float64)
+    dref = a.sum(0) + beta * db0.astype(np.float64)
+    return out.double().numpy(), ref, db, dref
+
+
+@pytest.mark.parametrize("M,N,K,beta,dt,with_ws", [
+    (768, 768, 16384, 0.0, 1, True),    # 256x128 tiles, 14 token splits: partial sums reduced with dW
+    (2304, 768, 4000, 1.0, 1, True),    # 256x256 tiles, split plan, ragged token tail, accumulate
+    (384, 200, 300, 1.0, 2, True),      # fp16, no split (written by the kernel), ragged rows and tokens
+    (200, 136, 97, 1.0, 1, False),      # no split-K workspace: generic kernel, column sums run apart
+    (96, 64, 130, 1.0, 0, True),        # fp32 operands: column sums run apart
+])
+def test_emu_weight_gradient_with_bias_gradient(L, M, N, K, beta, dt, with_ws):
+    """The bias gradient of a linear layer is the column sums of dY, the
+    weight-gradient GEMM's A operand; the TN kernel forms them from the A
+    fragments it already holds (split partials reduced with dW's), other
+    paths through the column-sum kernel.  The weight gradient is unchanged."""
+    got, ref, db, dref = _wgrad_bias(L, M, N, K, beta, dt, with_ws, seed=M + K)
+    close(got, ref, 1e-5, f"dW {M}x{N}x{K}")
+    close(db, dref, 1e-5, f"db {M}x{K}")
+
+
+def test_emu_bias_gradient_needs_unit_alpha(L):
+    z = torch.zeros(64 * 64, dtype=torch.bfloat16)
+    out = torch.zeros(64 * 64, dtype=torch.float32)
+    db = np.zeros(64, np.float32)
+    assert L.emu_gemm_wgrad_bias(64, 64, 64, ptr(z), 64, ptr(z), 64, ptr(out), 64, 0.5, 0.0, 1, None, 0,
+                                 ptr(db), None) != 0
 
 
 @slow
@@ -283,37 +362,6 @@ def test_emu_bias_column_sums(L, M, N, dt):
     db2 = db0.copy()
     assert L.emu_colsum(ptr(X), dt, M, N, N, ptr(db2), 0.0, ptr(part)) == 0
     close(db2, f64(X).sum(0), 1e-5, "column sums, beta 0")
-
-
-def test_emu_transpose_jobs_ragged(L):
-    """One launch transposes several 16-bit matrices of odd and ragged shapes
-    (tiles split over rows and columns, a 1 x 1 job, odd R and C), each into
-    its own region with a padded row stride; bitwise against numpy, the
-    padding and the gaps between regions untouched."""
-    shapes = [(3, 5), (130, 67), (64, 64), (1, 1), (200, 129)]
-    rng = np.random.default_rng(7)
-    src_parts, jobs, so, do, tile = [], [], 0, 0, 0
-    for R, C in shapes:
-        src_parts.append(rng.integers(0, 65536, size=R * C, dtype=np.uint16))
-        ldt = (R + 63) // 64 * 64 + 2
-        jobs.append((so, do + 6, R, C, ldt, tile))
-        so += R * C
-        do += 6 + C * ldt + 10
-        tile += ((R + 63) // 64) * ((C + 63) // 64)
-    src = np.concatenate(src_parts)
-    dst = np.full(do, 0x5A5A, dtype=np.uint16)
-    table = np.zeros(len(jobs), dtype=[("src", "<u8"), ("dst", "<u8"), ("R", "<i4"), ("C", "<i4"),
-                                       ("ldt", "<i4"), ("first", "<i4")])
-    for i, j in enumerate(jobs):
-        table[i] = j
-    assert table.itemsize == 32
-    assert L.emu_transpose_jobs(ptr(src), ptr(dst), ptr(table), len(jobs), tile) == 0
-    want = np.full(do, 0x5A5A, dtype=np.uint16)
-    for (s0, d0, R, C, ldt, _), part in zip(jobs, src_parts):
-        blk = np.full((C, ldt), 0x5A5A, dtype=np.uint16)
-        blk[:, :R] = part.reshape(R, C).T
-        want[d0:d0 + C * ldt] = blk.ravel()
-    assert np.array_equal(dst, want)
 
 
 # ---------------------------------------------------------------------------- attention

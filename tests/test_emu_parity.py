@@ -111,8 +111,8 @@ def test_emu_checkpoint_resume_bitwise(preset):
 
 
 @pytest.mark.parametrize("preset", ["bf16", "fp16"])
-def test_emu_transposed_copies_follow_weights(preset):
-    cases.transposed_copies_follow_weights(EMU, preset)
+def test_emu_weight_copies_follow_weights(preset):
+    cases.weight_copies_follow_weights(EMU, preset)
 
 
 def test_emu_arena_guard_detects_overrun():

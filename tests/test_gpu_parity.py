@@ -59,8 +59,8 @@ def test_checkpoint_resume_bitwise(preset):
 
 
 @pytest.mark.parametrize("preset", ["bf16", "fp16"])
-def test_transposed_copies_follow_weights(preset):
-    cases.transposed_copies_follow_weights(GPU, preset)
+def test_weight_copies_follow_weights(preset):
+    cases.weight_copies_follow_weights(GPU, preset)
 
 
 def test_arena_guard_detects_overrun():

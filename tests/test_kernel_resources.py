@@ -17,7 +17,7 @@ CSRC = os.path.join(ROOT, "decoder_only_transformer_02_amd", "csrc")
 HOT = ["k_gemm_nt", "k_gemm_tn", "k_gemm_f32m", "k_splitk_reduce", "k_attn_fwd64", "k_attn_dq64",
        "k_attn_dkv64", "k_xent", "k_loss_reduce", "k_ln_fwd", "k_ln_bwd", "k_ln_param_reduce", "k_colsum",
        "k_embed_fwd", "k_sort_runs", "k_merge_runs", "k_emb_seg", "k_dwpe", "k_sumsq", "k_norm_finalize",
-       "k_adamw", "k_transpose_jobs", "k_to_bf16", "k_to_f16", "k_kv_store", "k_attn_decode", "k_sample"]
+       "k_adamw", "k_to_bf16", "k_to_f16", "k_kv_store", "k_attn_decode", "k_sample"]
 
 # minimum waves per SIMD: (name part, floor, why)
 FLOORS = [
