@@ -1268,11 +1268,16 @@ static void launch_nt(GP q, hipStream_t st) {
   k_gemm_nt<TE, BM, BN, WM, WN, EPI, BKN><<<grid, WM * WN * 64, 0, st>>>(q);
 }
 
+// The direct-to-LDS kernels address an operand with 32-bit byte offsets
+// from its base: rows x ld 16-bit elements must stay below 4 GiB.
+static bool fits32(long rows, long ld) { return rows * ld * 2 < (1L << 32); }
+
 // The weight-gradient shapes the TN kernel takes (it also forms the bias
 // gradient, when asked, from the A fragments it holds).
 static bool tn_direct(const GemmArgs& a) {
   return (a.dt == ACT_BF16 || a.dt == ACT_F16) && a.kind == EPI_WGRAD && a.a_t && a.b_t && a.N % 4 == 0 &&
-         a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws;
+         a.ldo == a.N && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.splitk_ws && fits32(a.K, a.lda) &&
+         fits32(a.K, a.ldb);
 }
 
 template <typename TE, bool AT, bool BT, int EPI>
@@ -1304,7 +1309,8 @@ static hipError_t launch_h16(const GemmArgs& a, GP p, hipStream_t st) {
   // Forward (B = [N][K]) and dX (B = [K][N], N % 8 == 0): any K, the last
   // partial stage zero-filled.
   if constexpr (!AT && EPI != EPI_WGRAD) {
-    if (a.lda % 8 == 0 && a.ldb % 8 == 0 && (!BT || a.N % 8 == 0)) {
+    if (a.lda % 8 == 0 && a.ldb % 8 == 0 && (!BT || a.N % 8 == 0) && fits32(a.M, a.lda) &&
+        fits32(BT ? a.K : a.N, a.ldb)) {
       p.kchunk = a.K;
       switch (plan_nt(a.M, a.N)) {
         case 0: launch_nt<TE, 256, 256, 4, 2, EPI, BT>(p, st); break;
