@@ -460,19 +460,24 @@ def lr_at(it: int, max_lr=6e-4, warmup=132, max_steps=3400, min_ratio=0.1) -> fl
     return min_lr + 0.5 * (1.0 + math.cos(math.pi * ratio)) * (max_lr - min_lr)
 
 
-def train_step(P, micro_batches, cfg: Config, lr, clip=1.0, t=1, dt=F64, M_state=None, V_state=None):
+def train_step(P, micro_batches, cfg: Config, lr, clip=1.0, t=1, dt=F64, M_state=None, V_state=None,
+               progress=None):
     """micro_batches: list of (idx, targets).  Loss of each micro-batch is
     scaled by 1/len(micro_batches) and gradients summed, then one clipped
     AdamW step.  Returns dict with loss (mean of micro losses), grads (the
-    summed, unclipped ones), norm, coef, params, m, v."""
+    summed, unclipped ones), norm, coef, params, m, v.  `progress`, if
+    given, is called as progress(i, k) after micro-batch i of k (reporting
+    only; it takes no part in the arithmetic)."""
     k = len(micro_batches)
     total = None
     losses = []
-    for idx, tgt in micro_batches:
+    for i, (idx, tgt) in enumerate(micro_batches):
         loss, _, cache = forward(P, idx, tgt, cfg, dt)
         losses.append(loss)
         g = backward(P, cache, cfg, dt, grad_scale=1.0 / k)
         del cache
+        if progress is not None:
+            progress(i, k)
         if total is None:
             total = g
         else:

@@ -11,3 +11,5 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP library)")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+    from tests import gpu_helpers
+    gpu_helpers.PYTEST_CONFIG = config

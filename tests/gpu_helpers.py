@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import functools
 import sys
+import time
 
 import numpy as np
 
@@ -14,9 +15,33 @@ from decoder_only_transformer_02_amd import inputs
 from oracle import gpt2_oracle as O
 
 
+# pytest's config, set by conftest.py: lets say() write past output capture.
+PYTEST_CONFIG = None
+
+
 def say(*a):
-    print(*a, flush=True)
+    """Print a progress line on the real stdout, also while pytest captures
+    the test's output (a run without -s still shows that a long oracle
+    computation is advancing)."""
+    capman = PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if PYTEST_CONFIG else None
+    if capman is not None:
+        with capman.global_and_fixture_disabled():
+            print(*a, flush=True)
+    else:
+        print(*a, flush=True)
     sys.stdout.flush()
+
+
+def oracle_progress(label: str):
+    """A train_step progress callback: a line per oracle micro-batch once the
+    computation has run for more than 5 s (short ones stay quiet)."""
+    t0 = time.perf_counter()
+
+    def report(i, k):
+        dt = time.perf_counter() - t0
+        if dt > 5.0:
+            say(f"  oracle {label}: micro-batch {i + 1}/{k} done, {dt:.0f} s")
+    return report
 
 
 def configs(p: dict, B: int, T: int, **over):
@@ -127,7 +152,7 @@ def run_step(p, B, T, seed=0, data_seed=1, lr=6e-4, dt=np.float64, micro=1, be: 
     m.check_arena()
     m.close()
     P = oracle_init(oc, seed)
-    ref = O.train_step(P, batches, oc, lr=lr, clip=1.0, t=1, dt=dt)
+    ref = O.train_step(P, batches, oc, lr=lr, clip=1.0, t=1, dt=dt, progress=oracle_progress("step"))
     return float(np.mean(losses)), norm, gg, pp, ref
 
 

@@ -17,7 +17,8 @@ from decoder_only_transformer_02_amd import gpt2 as G
 from decoder_only_transformer_02_amd import inputs
 from oracle import gpt2_oracle as O
 from tests.gpu_helpers import (Backend, assert_bf16, assert_fp32, check_post_adamw, configs, cosine,
-                               gpu_grads, gpu_params, oracle_init, rel_l2, run_step, say, stream_for)
+                               gpu_grads, gpu_params, oracle_init, oracle_progress, rel_l2, run_step, say,
+                               stream_for)
 
 SMALL_BF16 = dict(n_layer=2, n_head=2, n_embd=128, block_size=128, vocab_size=1000,
                   padded_vocab=1000, compute="bf16", tokens="uniform")
@@ -473,7 +474,7 @@ def full_step_vs_oracle(be: Backend, preset: dict, B: int, T: int, lr: float = 6
     m.close()
     assert abs(loss - float(np.mean(per, dtype=np.float64))) <= 1e-5 * loss
     ref = O.train_step(oracle_init(oc, 0), _one_sequence_batches(x, y), oc, lr=lr, clip=1.0, t=1,
-                       dt=np.float32)
+                       dt=np.float32, progress=oracle_progress(f"B={B} T={T}"))
     assert_bf16(loss, norm, gg, pp, ref, lr=lr)
 
 
@@ -498,7 +499,7 @@ def full_step_fp32_vs_oracle(be: Backend, B: int, T: int, n_layer=None):
     m.check_arena()
     m.close()
     ref = O.train_step(oracle_init(oc, 0), _one_sequence_batches(x, y), oc, lr=6e-4, clip=1.0, t=1,
-                       dt=np.float32)
+                       dt=np.float32, progress=oracle_progress(f"fp32 B={B} T={T}"))
     say("loss", loss, ref["loss"], "norm", norm, ref["norm"])
     assert abs(loss - ref["loss"]) <= 1e-4 * ref["loss"]
     assert abs(norm - ref["norm"]) <= 1e-4 * ref["norm"]
@@ -535,7 +536,8 @@ def accumulated_step_vs_oracle(be: Backend, B: int = 32, T: int = 512, micro: in
     seqs = []
     for x, y in batches:
         seqs += _one_sequence_batches(x, y)
-    ref = O.train_step(oracle_init(oc, 0), seqs, oc, lr=lr, clip=1.0, t=1, dt=np.float32)
+    ref = O.train_step(oracle_init(oc, 0), seqs, oc, lr=lr, clip=1.0, t=1, dt=np.float32,
+                       progress=oracle_progress(f"{micro} x B={B} T={T}"))
     assert_bf16(float(np.mean(losses)), norm, gg, pp, ref, lr=lr)
 
 
