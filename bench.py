@@ -7,14 +7,17 @@ Prints one JSON line:
     median / p10 / p90 of per-step HIP-event times on the library stream;
   * mfu: (6N + 6 L C (T+1)) flops per token against the bf16 dense peak;
   * roofline: the dominant kernel (the classifier forward GEMM), its
-    algorithmic flops over its HIP-event launch time;
+    algorithmic flops over its launch time, from HIP events around each of
+    its launches during the timed steps;
   * kernels: every timing class of the library with its algorithmic work
     per step (the scope table's per-unit figures times the units of one
     step), its time per step and its fraction of the MI355X roofline;
   * padding: the classifier GEMMs + cross-entropy and the whole step at the
     unpadded vocabulary 50257 against the padded 50304;
   * accumulated_step: one optimizer step of 32 micro-steps of B=32, T=512
-    (524,288 tokens) with clip and AdamW at lr(132);
+    (524,288 tokens) with clip and AdamW at lr(132), median of 10;
+  * block: one transformer block's forward and backward alone at B=16,
+    T=1024, median of 20;
   * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 Inputs are resident in device memory before every timed region.
 """
@@ -89,9 +92,10 @@ def roofline_entry(bound, work, ms):
             "frac": round(ach * 1e9 / PEAK_HBM, 4)}
 
 
-def cpu_baseline(preset):
-    """The oracle as it stands, one full step on one sequence of T tokens of
-    the same model (a bounded sample of the benchmark batch)."""
+def cpu_baseline(preset, n_seq=2):
+    """The oracle as it stands, one full step of the same model on `n_seq`
+    sequences of T tokens (a bounded sample of the benchmark batch, taken as
+    one-sequence micro-batches, as the parity tests take it)."""
     import numpy as np
     from decoder_only_transformer_02_amd import inputs
     from oracle import gpt2_oracle as O
@@ -104,17 +108,53 @@ def cpu_baseline(preset):
                   preset["vocab_size"], preset["padded_vocab"])
     P = O.init_params(oc, 0)
     T = preset["T"]
-    x, y = inputs.batch_from_stream(inputs.zipf_stream(0, T + 1, preset["vocab_size"]), 1, T)
+    x, y = inputs.batch_from_stream(inputs.zipf_stream(0, n_seq * T + 1, preset["vocab_size"]), n_seq, T)
     t0 = time.perf_counter()
-    O.train_step(P, [(x, y)], oc, lr=6e-4, clip=1.0, t=1, dt=np.float32)
+    O.train_step(P, [(x[b:b + 1], y[b:b + 1]) for b in range(n_seq)], oc, lr=6e-4, clip=1.0, t=1,
+                 dt=np.float32)
     dt = time.perf_counter() - t0
     cores = blas_threads or len(os.sched_getaffinity(0))
-    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one full step (forward, backward, clip, AdamW) of the same model on one sequence "
-                      f"of {T} tokens (1/{preset['B']} of the benchmark batch), float32 storage with "
+    return {"value": round(n_seq * T / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full step (forward, backward, clip, AdamW) of the same model on {n_seq} sequences "
+                      f"of {T} tokens ({n_seq}/{preset['B']} of the benchmark batch), float32 storage with "
                       f"float64 reductions, {dt:.1f} s; host has {os.cpu_count()} CPUs, "
                       f"{len(os.sched_getaffinity(0))} in this process's affinity, BLAS threads "
                       f"{blas_threads}"}
+
+
+def block_leg(G, inputs, torch, runs=20, warmup=3):
+    """One transformer block in isolation (forward and backward of layer 0,
+    bf16): the median of `runs` HIP-event timed calls, with its algorithmic
+    work: the 12 GEMMs (3 x 2 M 12 C^2) and the causal attention forward and
+    backward (3 x 4 hd flops per score, T(T+1)/2 scores per head)."""
+    pb = inputs.PRESETS["block124m"]
+    B, T, C, H = pb["B"], pb["T"], pb["n_embd"], pb["n_head"]
+    cfg = G.make_config(**{**pb, "max_batch": B, "max_seq": T})
+    m = G.GPT2Step(cfg, seed=0)
+    x, dy = inputs.block_inputs(0, B, T, C)
+    x = torch.from_numpy(x).cuda()
+    dy = torch.from_numpy(dy).cuda()
+    for _ in range(warmup):
+        m.block_fwd_bwd(0, x, dy)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for a, b in ev:
+        a.record()
+        m.block_fwd_bwd(0, x, dy)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    m.close()
+    torch.cuda.synchronize()
+    M = B * T
+    gemm = 3 * 2 * M * 12 * C * C
+    attn = 3 * B * H * (T * (T + 1) // 2) * (C // H) * 4
+    med = percentile(ms, 50)
+    e = roofline_entry("mfma", gemm + attn, med)
+    return {"workload": f"one 124M block, forward and backward, B={B}, T={T}, bf16", "runs": runs,
+            "ms_median": round(med, 4), "ms_p10": round(percentile(ms, 10), 4),
+            "ms_p90": round(percentile(ms, 90), 4), "flops": gemm + attn, "tokens_per_s": round(M / (med * 1e-3), 1),
+            "achieved_tflops": e["achieved"], "frac_of_bf16_peak": e["frac"]}
 
 
 class Runner:
@@ -142,13 +182,20 @@ class Runner:
             self.m.backward(1.0 / k)
         self.m.step(lr, 1.0, sync=False)
 
-    def timed(self, steps, warmup, lr=6e-4):
+    def timed(self, steps, warmup, lr=6e-4, kernel_class=None):
         """Wall-clock seconds of exactly `steps` steps between two device
-        synchronizations, and the per-step HIP-event times (ms)."""
+        synchronizations, and the per-step HIP-event times (ms).  With
+        `kernel_class`, the library also brackets that class's launches with
+        HIP events on its stream during the timed steps; the summed time
+        and launch count are kept in self.class_timed."""
         torch = self.torch
+        if kernel_class:
+            self.m.timing_enable(kernel_class)   # warm-up creates the events
         for _ in range(warmup):
             self.step(lr)
         torch.cuda.synchronize()
+        if kernel_class:
+            self.m.timing_read()                 # drop the warm-up brackets
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
@@ -159,6 +206,9 @@ class Runner:
             b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if kernel_class:
+            self.class_timed = self.m.timing_read()
+            self.m.timing_enable("none")
         return wall, [a.elapsed_time(b) for a, b in ev]
 
     def class_ms(self, cls, steps=3):
@@ -178,8 +228,8 @@ class Runner:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the unpadded-vocabulary and accumulated-step measurements")
@@ -199,7 +249,8 @@ def main():
     print(f"config 124M B={B} T={T}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr,
           flush=True)
     r = Runner(G, inputs, torch, p)
-    wall, ev_ms = r.timed(args.steps, args.warmup)
+    wall, ev_ms = r.timed(args.steps, args.warmup, kernel_class="lmhead_fwd")
+    lm_ms, lm_n = r.class_timed
     ms = wall / args.steps * 1e3
     tokens = B * T * args.steps / wall
     n_total = G.lib().gpt2_num_params(ctypes.byref(r.cfg))
@@ -222,7 +273,8 @@ def main():
     r.close()
     del r
 
-    lm = kernels["lmhead_fwd"]
+    # the dominant kernel's rate over the timed steps themselves
+    lm = roofline_entry("mfma", work["lmhead_fwd"][1], lm_ms / max(args.steps, 1))
     out = {
         "metric": METRIC,
         "value": round(tokens, 1),
@@ -248,8 +300,10 @@ def main():
         "roofline": {"kernel": "classifier GEMM forward (k_gemm_nt 256x256, EPI_LOGITS)",
                      "bound": "mfma", "achieved": lm["achieved"], "peak": lm["peak"], "unit": "TFLOP/s",
                      "frac": lm["frac"], "traffic": None,
-                     "avg_launch_ms": round(lm["ms_per_step"] / max(lm["launches_per_step"], 1), 4),
-                     "launches": lm["launches_per_step"]},
+                     "avg_launch_ms": round(lm_ms / max(lm_n, 1), 4),
+                     "launches": lm_n / max(args.steps, 1),
+                     "timed_over": f"HIP events on the library stream around each classifier launch "
+                                   f"of the {args.steps} timed steps"},
         "kernels": kernels,
     }
 
@@ -272,17 +326,22 @@ def main():
         print("accumulated step (32 x B=32 T=512)", file=sys.stderr, flush=True)
         pa = inputs.PRESETS["gpt2_124m_accum"]
         a = Runner(G, inputs, torch, pa, micro=pa["accum"])
-        a_wall, a_ev = a.timed(3, 1, lr=G.lr_at(pa["lr_step"]))
+        a_steps = 10
+        a_wall, a_ev = a.timed(a_steps, 3, lr=G.lr_at(pa["lr_step"]))
         a.close()
         del a
         a_tok = pa["B"] * pa["T"] * pa["accum"]
         a_ms = percentile(a_ev, 50)
         out["accumulated_step"] = {
-            "tokens_per_step": a_tok, "ms_per_step_median": round(a_ms, 2),
-            "ms_per_step_wall_mean": round(a_wall / 3 * 1e3, 2),
+            "tokens_per_step": a_tok, "steps": a_steps, "warmup": 3, "ms_per_step_median": round(a_ms, 2),
+            "ms_per_step_p10": round(percentile(a_ev, 10), 2), "ms_per_step_p90": round(percentile(a_ev, 90), 2),
+            "ms_per_step_wall_mean": round(a_wall / a_steps * 1e3, 2),
             "tokens_per_s": round(a_tok / (a_ms * 1e-3), 1),
             "mfu": round(a_tok / (a_ms * 1e-3) * flops_per_token(pa["n_layer"], pa["n_embd"], pa["T"], n_mfu)
                          / PEAK_BF16, 4)}
+    if not args.no_extra:
+        print("single block (B=16 T=1024)", file=sys.stderr, flush=True)
+        out["block"] = block_leg(G, inputs, torch)
     if not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p)

@@ -70,8 +70,9 @@ def test_roofline_entry_and_percentiles():
 def test_bench_control_flow_on_the_emulated_library(monkeypatch, capsys):
     """bench.main() end to end with the library's CPU emulation standing in
     for the GPU and small presets standing in for the 124M shapes: every leg
-    runs (timed steps, per-class timing, unpadded vocabulary, accumulated
-    step, oracle baseline) and one JSON line with the contract's keys is
+    runs (timed steps with the classifier's launches bracketed, per-class
+    timing, unpadded vocabulary, accumulated step, single block, oracle
+    baseline) and one JSON line with the contract's keys is
     printed.  Timings here mean nothing; only the control flow is checked."""
     import json
     import time as _time
@@ -94,7 +95,8 @@ def test_bench_control_flow_on_the_emulated_library(monkeypatch, capsys):
     small = dict(n_layer=2, n_head=2, n_embd=128, block_size=64, vocab_size=1000, padded_vocab=1024,
                  B=2, T=32, compute="bf16", tokens="zipf")
     presets = {"gpt2_124m": small, "gpt2_124m_v50257": {**small, "padded_vocab": 1000},
-               "gpt2_124m_accum": {**small, "B": 2, "T": 16, "accum": 2, "lr_step": 132}}
+               "gpt2_124m_accum": {**small, "B": 2, "T": 16, "accum": 2, "lr_step": 132},
+               "block124m": {**small, "tokens": "none"}}
     monkeypatch.setattr(inputs, "PRESETS", presets)
     monkeypatch.setattr(G, "GPT2Step", EmuStep)
     monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
@@ -106,7 +108,8 @@ def test_bench_control_flow_on_the_emulated_library(monkeypatch, capsys):
     rec = json.loads(line)
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
                 "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "kernels",
-                "padding", "accumulated_step", "ms_per_step_median", "ms_per_step_p10", "ms_per_step_p90"):
+                "padding", "accumulated_step", "block", "ms_per_step_median", "ms_per_step_p10",
+                "ms_per_step_p90"):
         assert key in rec, key
     assert rec["metric"] == bench.METRIC and rec["steps"] == 3 and rec["n_gpus"] == 1
     assert rec["roofline"]["bound"] == "mfma" and rec["roofline"]["launches"] == 1
@@ -116,4 +119,5 @@ def test_bench_control_flow_on_the_emulated_library(monkeypatch, capsys):
     assert "transpose" not in rec["kernels"] and "colsum" not in rec["kernels"]
     assert rec["kernels"]["ln_fwd"]["launches_per_step"] == 2 * small["n_layer"] + 1
     assert rec["cpu_baseline"]["kind"] == "oracle" and rec["cpu_baseline"]["cores"] >= 1
-    assert rec["accumulated_step"]["tokens_per_step"] == 2 * 16 * 2
+    assert rec["accumulated_step"]["tokens_per_step"] == 2 * 16 * 2 and rec["accumulated_step"]["steps"] == 10
+    assert rec["block"]["runs"] == 20 and rec["block"]["ms_median"] > 0
