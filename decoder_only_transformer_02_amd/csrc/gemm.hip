@@ -407,6 +407,11 @@ __device__ __forceinline__ void stage_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Compiler scheduling fence (emits no instruction): nothing is moved across
+// it, so the fragment reads and MFMA groups keep their software-pipelined
+// order instead of the scheduler's register-saving one.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from base + soff + voff into LDS at lds + 16 * lane.
@@ -554,6 +559,16 @@ __device__ __forceinline__ void tok_tail(const uint16_t* __restrict__ g, long ld
   }
 }
 
+// One LDS transpose read.  Taken through a restrict-qualified pointer, the
+// read carries alias-scope information, and the compiler then no longer
+// drains every in-flight buffer-to-LDS load (vmcnt 0) before it, which would
+// cut the load ring to depth one.  The kernels order these reads against
+// the ring loads themselves: each wave waits (vmcnt) for its loads of a
+// stage, then the block barrier makes the stage visible to all waves.
+__device__ __forceinline__ v4s lds_read_tr(const uint16_t* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+}
+
 // 8 k values (rows ks*16 + 8g .. +7) of column `col` of an LDS tile
 // [32][COLS], as an MFMA operand; lane l serves column cbase + l % 32.
 template <int COLS>
@@ -565,7 +580,7 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int cbase, int ks
   for (int hh = 0; hh < 2; ++hh) {
     const int m = ks * 16 + 8 * (G >> 1) + 4 * hh + (q >> 2);
     const int off = m * COLS + (((col >> 3) ^ tok_swz<COLS>(m)) << 3) + (col & 7);
-    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off));
+    h[hh] = lds_read_tr(tile + off);
   }
   return make_uint4(__builtin_bit_cast(uint32_t, (short2){h[0][0], h[0][1]}),
                     __builtin_bit_cast(uint32_t, (short2){h[0][2], h[0][3]}),
@@ -689,9 +704,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
         acc[i][j] = H16<TE>::mfma(bfr[set][j], af[set][i], acc[i][j]);
   };
 
-  // Stage s + 1 is made visible (wait + barrier) one stage early, so the
-  // first fragments of the next stage are read before the barrier and only
-  // the barrier itself separates the two MFMA groups of a stage.
+  // Stage s + 2 is made visible (wait + barrier) one stage early, so the
+  // first fragments of the next stage are read during this stage's second
+  // MFMA group.  The barrier comes after that group: the LDS drain it
+  // needs (this wave's fragment reads of stage s, whose slot the next
+  // issue refills) then overlaps the MFMAs instead of stalling them.
   if (total > 0) {
     const int pro = min(NS - 1, total);
     for (int t = 0; t < pro; ++t) issue_next(t);
@@ -703,12 +720,21 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   for (int round = 0; round < my_n; ++round) {
     for (int kt = 0; kt < nk; ++kt, ++s) {
       if (s + NS - 1 < total) issue_next(s + NS - 1);
+      // Software pipeline of the fragment reads, kept in this order by
+      // compiler scheduling fences: each MFMA group consumes fragments read
+      // one group earlier.  The next stage's reads are unconditional (a
+      // read of a ring slot is always in bounds; on the last stage its
+      // values are unused): a conditional read would make the wait before
+      // the second group count it as possibly absent and drain it too.
       load_frags(s, 1, 1);
+      sched_fence();
       mfma_set(0);
-      if (s + 1 < total) load_frags(s + 1, 0, 0);
+      sched_fence();
+      load_frags(s + 1, 0, 0);
+      sched_fence();
+      mfma_set(1);
       if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
       stage_barrier();
-      mfma_set(1);
     }
     int tm, tn;
     grouped_coords(tile_pid(round, G), nm, nn, tm, tn);
@@ -876,14 +902,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tn(GP p) {
     const bool sums = p.dbias != nullptr && tn == 0 && wn == 0;  // uniform per wave
     for (int kt = 0; kt < nk; ++kt, ++s) {
       if (s + NS - 1 < total) issue_next(s + NS - 1);
-      load_frags(s, 1, 1);
+      load_frags(s, 1, 1);  // the same software pipeline as k_gemm_nt
+      sched_fence();
       mfma_set(0);
       if (sums) add_sums(0);
-      if (s + 1 < total) load_frags(s + 1, 0, 0);
-      if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
-      stage_barrier();
+      sched_fence();
+      load_frags(s + 1, 0, 0);
+      sched_fence();
       mfma_set(1);
       if (sums) add_sums(1);
+      // after the second MFMA group, as in k_gemm_nt
+      if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
+      stage_barrier();
     }
     const int m0 = tm * BM, n0 = tn * BN;
     if (sums) {

@@ -268,6 +268,8 @@ inline void __syncthreads() { ::emu::syncthreads(); }
   ::emu::buffer_load_lds(r, (void*)(l), sz, vo, so, of, ax)
 #define __builtin_amdgcn_s_waitcnt(imm) ::emu::waitcnt(imm)
 #define __builtin_amdgcn_s_barrier() ::emu::barrier()
+// compiler scheduling fence: no effect on what the code computes
+#define __builtin_amdgcn_sched_barrier(mask) ((void)0)
 #define __builtin_amdgcn_perm(a, b, s) ::emu::perm(a, b, s)
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
 #define __builtin_amdgcn_rcpf(x) (1.0f / (x))
