@@ -1,0 +1,98 @@
+"""Static checks of the gfx950 machine code that build() produced for the
+GEMM kernels (the disassembly of the library's own gemm.hip object; no GPU).
+
+The 16-bit GEMMs fill an LDS ring with buffer-to-LDS loads several stages
+ahead and order their LDS reads against those loads themselves (each wave
+waits for its own loads of a stage, then the block barrier).  The compiler
+inserts a wait for every in-flight load (s_waitcnt vmcnt(0)) before an LDS
+read that it cannot tell apart from the loads' LDS writes, as it did for
+the transpose reads of the weight-gradient and dX kernels: that cuts the
+ring to depth one and exposes a memory latency at every stage, and nothing
+but the machine code shows it."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OBJ = os.path.join(ROOT, "_build", "gemm.o")
+SRC = os.path.join(ROOT, "decoder_only_transformer_02_amd", "csrc", "gemm.hip")
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _tool(name):
+    p = os.path.join(LLVM, name)
+    return p if os.path.exists(p) else shutil.which(name)
+
+
+@pytest.fixture(scope="module")
+def disassembly(tmp_path_factory):
+    tools = [_tool(n) for n in ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")]
+    if not all(tools):
+        pytest.skip("ROCm LLVM tools not found")
+    if not os.path.exists(OBJ):
+        pytest.skip("no build: run __graft_entry__.build() first")
+    if os.path.getmtime(OBJ) < os.path.getmtime(SRC):
+        pytest.skip("the build is older than gemm.hip: run __graft_entry__.build() again")
+    objcopy, bundler, objdump = tools
+    d = tmp_path_factory.mktemp("gemm_isa")
+    fat, co = str(d / "fatbin"), str(d / "gfx950.co")
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", OBJ], check=True)
+    subprocess.run([bundler, "--unbundle", "--type=o", f"--input={fat}",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True)
+    r = subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True, capture_output=True, text=True)
+    return r.stdout
+
+
+def kernels(text):
+    """Kernel symbol -> its instructions (mnemonic and operands, without the
+    address and encoding comment)."""
+    out, cur = {}, None
+    for line in text.split("\n"):
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:$", line)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+            continue
+        t = line.split("//")[0].strip()
+        if cur is not None and t:
+            cur.append(t)
+    return out
+
+
+def ring_drains(instrs):
+    """Places where a full vector-memory wait directly precedes an LDS read
+    (s_nop padding ignored)."""
+    n, prev = 0, None
+    for t in instrs:
+        if t.startswith("s_nop"):
+            continue
+        if prev is not None and re.match(r"s_waitcnt\b.*\bvmcnt\(0\)", prev) and t.startswith("ds_read"):
+            n += 1
+        prev = t
+    return n
+
+
+def test_disassembly_has_the_ring_gemms(disassembly):
+    ks = kernels(disassembly)
+    tn = [k for k in ks if "k_gemm_tn" in k]
+    bkn = [k for k in ks if "k_gemm_nt" in k and k.endswith("ELb1EEEvNS_2GPE")]
+    assert len(tn) >= 3 and len(bkn) >= 6, (len(tn), len(bkn))
+
+
+def test_no_load_ring_drain_before_lds_reads(disassembly):
+    ks = kernels(disassembly)
+    bad = {k: ring_drains(v) for k, v in ks.items() if re.search(r"k_gemm_(nt|tn)I", k)}
+    bad = {k: n for k, n in bad.items() if n}
+    assert not bad, bad
+
+
+def test_the_check_sees_a_drain():
+    """The detector itself, on the instruction pattern the compiler had
+    emitted before the transpose reads carried alias-scope information."""
+    assert ring_drains(["buffer_load_dwordx4 v1, s[4:7], 0 offen lds", "s_waitcnt vmcnt(0)",
+                        "ds_read_b64_tr_b16 v[2:3], v4"]) == 1
+    assert ring_drains(["s_waitcnt vmcnt(4)", "ds_read_b128 v[0:3], v4"]) == 0
+    assert ring_drains(["s_waitcnt vmcnt(0)", "s_nop 0", "ds_read_b128 v[0:3], v4"]) == 1
+    assert ring_drains(["s_waitcnt lgkmcnt(0)", "ds_read_b128 v[0:3], v4"]) == 0
