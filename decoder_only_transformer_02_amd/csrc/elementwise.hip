@@ -658,13 +658,22 @@ __global__ __launch_bounds__(256) void k_xent(T* __restrict__ logits, int ld, in
   const int kown = ych / 256, town = ych % 256, yo = y - ych * E;  // the target's chunk: pass, thread, slot
   if ((int)threadIdx.x == town) sh_zy = to_f(z[y]);
   uint4 buf[NCH];
-  // The tests on k alone are uniform (scalar branches): only the last
-  // passes, whose chunks can reach ld or V, pay for the per-thread tests.
+  // Every load first, without branches, so that the row's loads are all in
+  // flight together: a load under a branch leaves a register copy where the
+  // paths join, and that copy waits for the load before the next one is
+  // issued.  A chunk at or past ld reads the row's first chunk instead (in
+  // bounds) and is replaced below.  The tests on k alone are uniform
+  // (scalar branches): only the last passes, whose chunks can reach ld or
+  // V, pay for the per-thread tests.
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int e0 = (threadIdx.x + k * 256) * E;
-    if ((k + 1) * 256 * E <= ld) buf[k] = *(const uint4*)(z + e0);
-    else buf[k] = e0 < ld ? *(const uint4*)(z + e0) : chunk_neginf<T>();
+    buf[k] = *(const uint4*)(z + (e0 < ld ? e0 : 0));
+  }
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int e0 = (threadIdx.x + k * 256) * E;
+    if ((k + 1) * 256 * E > ld && e0 >= ld) buf[k] = chunk_neginf<T>();
     if ((k + 1) * 256 * E > V && e0 + E > V) buf[k] = chunk_keep<T>(buf[k], V - e0);  // n <= 0: all -inf
   }
   float mx = -INFINITY;

@@ -1,5 +1,6 @@
-"""Static checks of the gfx950 machine code that build() produced for the
-GEMM kernels (the disassembly of the library's own gemm.hip object; no GPU).
+"""Static checks of the gfx950 machine code that build() produced (the
+disassembly of the library's own objects; no GPU): the GEMMs' load ring and
+the cross-entropy's row loads.
 
 The 16-bit GEMMs fill an LDS ring with buffer-to-LDS loads several stages
 ahead and order their LDS reads against those loads themselves (each wave
@@ -17,8 +18,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OBJ = os.path.join(ROOT, "_build", "gemm.o")
-SRC = os.path.join(ROOT, "decoder_only_transformer_02_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "decoder_only_transformer_02_amd", "csrc")
 LLVM = "/opt/rocm/llvm/bin"
 
 
@@ -27,23 +27,34 @@ def _tool(name):
     return p if os.path.exists(p) else shutil.which(name)
 
 
-@pytest.fixture(scope="module")
-def disassembly(tmp_path_factory):
+def _disassemble(src, d):
+    """gfx950 disassembly of the device code in _build/<src>.o."""
     tools = [_tool(n) for n in ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")]
     if not all(tools):
         pytest.skip("ROCm LLVM tools not found")
-    if not os.path.exists(OBJ):
+    obj = os.path.join(ROOT, "_build", src.replace(".hip", ".o"))
+    if not os.path.exists(obj):
         pytest.skip("no build: run __graft_entry__.build() first")
-    if os.path.getmtime(OBJ) < os.path.getmtime(SRC):
-        pytest.skip("the build is older than gemm.hip: run __graft_entry__.build() again")
+    newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in os.listdir(CSRC))
+    if os.path.getmtime(obj) < newest:
+        pytest.skip("the build is older than the sources: run __graft_entry__.build() again")
     objcopy, bundler, objdump = tools
-    d = tmp_path_factory.mktemp("gemm_isa")
-    fat, co = str(d / "fatbin"), str(d / "gfx950.co")
-    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", OBJ], check=True)
+    fat, co = str(d / (src + ".fatbin")), str(d / (src + ".co"))
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", obj], check=True)
     subprocess.run([bundler, "--unbundle", "--type=o", f"--input={fat}",
                     "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True)
     r = subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True, capture_output=True, text=True)
     return r.stdout
+
+
+@pytest.fixture(scope="module")
+def disassembly(tmp_path_factory):
+    return _disassemble("gemm.hip", tmp_path_factory.mktemp("gemm_isa"))
+
+
+@pytest.fixture(scope="module")
+def disassembly_elementwise(tmp_path_factory):
+    return _disassemble("elementwise.hip", tmp_path_factory.mktemp("elementwise_isa"))
 
 
 def kernels(text):
@@ -96,3 +107,41 @@ def test_the_check_sees_a_drain():
     assert ring_drains(["s_waitcnt vmcnt(4)", "ds_read_b128 v[0:3], v4"]) == 0
     assert ring_drains(["s_waitcnt vmcnt(0)", "s_nop 0", "ds_read_b128 v[0:3], v4"]) == 1
     assert ring_drains(["s_waitcnt lgkmcnt(0)", "ds_read_b128 v[0:3], v4"]) == 0
+
+
+def serialized_loads(instrs):
+    """Global loads that wait for every earlier load (s_waitcnt vmcnt(0))
+    with no other load between: the pattern of loads issued one at a time."""
+    seq = []
+    for t in instrs:
+        if t.startswith("global_load") or (t.startswith("buffer_load") and " lds" not in t):
+            seq.append("G")
+        elif re.match(r"s_waitcnt\b.*\bvmcnt\(0\)", t):
+            seq.append("W")
+    s = "".join(seq)
+    return sum(1 for i in range(len(s) - 2) if s[i:i + 3] == "GWG")
+
+
+def test_cross_entropy_row_loads_are_in_flight_together(disassembly_elementwise):
+    """The register-resident cross-entropy loads its whole row (up to 25
+    chunks of 16 bytes per thread) before it waits.  With the loads under
+    per-chunk branches, the compiler had issued them one at a time (a
+    register copy at each branch join waited for the load), 25 memory
+    latencies per row."""
+    ks = kernels(disassembly_elementwise)
+    xent = {k: v for k, v in ks.items() if re.search(r"k_xentI.*Li(2|4|8|16|25)E", k)}
+    assert len(xent) >= 15, len(xent)
+    bad = {k: serialized_loads(v) for k, v in xent.items()}
+    # a prologue load or two (target id, loss scale) may wait; the row's
+    # loads one at a time gave one per chunk (4 to 25 here)
+    bad = {k: n for k, n in bad.items() if n > 2}
+    assert not bad, bad
+
+
+def test_the_serialization_check_sees_one():
+    assert serialized_loads(["global_load_dwordx4 v[0:3], v8, s[2:3]", "s_waitcnt vmcnt(0)",
+                             "v_mov_b32 v4, v0", "global_load_dwordx4 v[0:3], v9, s[2:3]",
+                             "s_waitcnt vmcnt(0)", "global_load_dwordx4 v[0:3], v10, s[2:3]"]) == 2
+    assert serialized_loads(["global_load_dwordx4 v[0:3], v8, s[2:3]",
+                             "global_load_dwordx4 v[4:7], v9, s[2:3]", "s_waitcnt vmcnt(1)",
+                             "s_waitcnt vmcnt(0)"]) == 0
