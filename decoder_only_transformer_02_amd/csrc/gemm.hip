@@ -569,6 +569,10 @@ __device__ __forceinline__ v4s lds_read_tr(const uint16_t* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
 }
 
+// Four bias values staged in LDS, read like lds_read_tr (alias-scoped, so
+// the compiler does not drain the ring's in-flight loads before it).
+__device__ __forceinline__ float4 lds_read_bias4(const float* __restrict__ p) { return *(const float4*)p; }
+
 // 8 k values (rows ks*16 + 8g .. +7) of column `col` of an LDS tile
 // [32][COLS], as an MFMA operand; lane l serves column cbase + l % 32.
 template <int COLS>
@@ -617,7 +621,17 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   static_assert(NK == TK, "A and B stages cover the same k");
   constexpr int STAGE = (BM + BN) * NK;  // 16-bit elements per stage
   constexpr int PER = BufLoader<BM, NW>::NI + LoaderB::NI;  // loads per stage
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+  // The bias vector, staged in LDS once per workgroup when it fits: the
+  // epilogues then read it without vector-memory loads.  Such a load in
+  // the epilogue has to be waited for, and the wait (one counter for loads
+  // and stores) also drains every store the epilogue has issued so far.
+  // It sits at the end of the ring's array: a second LDS variable would
+  // give the accesses alias scopes, and the compiler would then drain the
+  // in-flight ring loads before the ring's fragment reads.
+  constexpr bool EPI_HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr int BIAS_MAX = EPI_HAS_BIAS ? 4096 : 0;  // floats
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE + 2 * BIAS_MAX];
+  float* const bias_s = (float*)(lds + NS * STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = (wv / WN) * TM, wn = (wv % WN) * TN;
@@ -709,15 +723,59 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
   // MFMA group.  The barrier comes after that group: the LDS drain it
   // needs (this wave's fragment reads of stage s, whose slot the next
   // issue refills) then overlaps the MFMAs instead of stalling them.
+  const bool lds_bias = EPI_HAS_BIAS && p.bias != nullptr && p.N <= BIAS_MAX && (p.N & 3) == 0;  // uniform
   if (total > 0) {
     const int pro = min(NS - 1, total);
     for (int t = 0; t < pro; ++t) issue_next(t);
+    if constexpr (EPI_HAS_BIAS) {
+      // after the ring's first loads, so their latencies overlap.  No
+      // branch around the loads or the stores (a branch lets the compiler
+      // sink each load next to its store and wait for it alone): a chunk
+      // past N loads the vector's first chunk, and its slot is never read.
+      if (lds_bias) {
+        constexpr int NB = BIAS_MAX / (NW * 64 * 4);
+        static_assert(NB >= 1 && NB * NW * 64 * 4 == BIAS_MAX, "one slot per chunk");
+        float4 bv[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int c = (tid + i * NW * 64) * 4;
+          bv[i] = *(const float4*)(p.bias + (c < p.N ? c : 0));
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) *(float4*)&bias_s[(tid + i * NW * 64) * 4] = bv[i];
+      }
+    }
     wait_stage(min(1, total - 1), pro - 1);
-    stage_barrier();
+    stage_barrier();  // also publishes bias_s
     load_frags(0, 0, 0);
   }
   int s = 0;
   for (int round = 0; round < my_n; ++round) {
+    int tm, tn;
+    grouped_coords(tile_pid(round, G), nm, nn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;  // whole tile inside the output
+    if constexpr (EPI == EPI_RESID) {
+      // The residual stream enters the accumulators before the tile's MFMAs
+      // (they then add the products to it), so the epilogue has no loads to
+      // wait for.  With one tile per workgroup (the 768-wide outputs) these
+      // loads overlap the ring's first stages.
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const size_t o = (size_t)(m0 + wm + i * 32 + fr) * p.ldo + n0 + wn + j * 32 + e4 * 8 + g * 4;
+              const float4 x = *(const float4*)((const float*)p.aux + o);
+              acc[i][j][e4 * 4 + 0] = x.x;
+              acc[i][j][e4 * 4 + 1] = x.y;
+              acc[i][j][e4 * 4 + 2] = x.z;
+              acc[i][j][e4 * 4 + 3] = x.w;
+            }
+      }
+    }
     for (int kt = 0; kt < nk; ++kt, ++s) {
       if (s + NS - 1 < total) issue_next(s + NS - 1);
       // Software pipeline of the fragment reads, kept in this order by
@@ -736,21 +794,74 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_nt(GP p) {
       if (s + 2 < total) wait_stage(s + 2, min(s + NS - 1, total - 1));
       stage_barrier();
     }
-    int tm, tn;
-    grouped_coords(tile_pid(round, G), nm, nn, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    if (m0 + BM <= p.M && n0 + BN <= p.N) {  // whole tile inside the output
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
-          const float4 b = epi_bias4<EPI>(p, c);
+    if (full) {
+      if constexpr (EPI == EPI_DGELU) {
+        // The u values in groups of (column block, 4-column run), PD groups
+        // ahead of the group being stored: each wait then leaves the later
+        // loads and the stores already issued in flight.
+        constexpr int NG = FN * 4, PD0 = 16 / FM, PD = PD0 < 1 ? 1 : (PD0 > NG ? NG : PD0);
+        uint2 ub[NG][FM];
+        auto load_u = [&](int gi) {
+          const int c = n0 + wn + (gi >> 2) * 32 + (gi & 3) * 8 + g * 4;
 #pragma unroll
           for (int i = 0; i < FM; ++i)
-            epi_store4_full<EPI, TE>(p, m0 + wm + i * 32 + fr, c, b, acc[i][j][e4 * 4 + 0],
-                                     acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+            ub[gi][i] = *(const uint2*)((const TE*)p.aux + (size_t)(m0 + wm + i * 32 + fr) * p.ldo + c);
+        };
+#pragma unroll
+        for (int gi = 0; gi < PD; ++gi) load_u(gi);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          if (gi + PD < NG) load_u(gi + PD);
+          const int j = gi >> 2, e4 = gi & 3;
+          const int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const uint2 uu = ub[gi][i];
+            const float v0 = acc[i][j][e4 * 4 + 0], v1 = acc[i][j][e4 * 4 + 1];
+            const float v2 = acc[i][j][e4 * 4 + 2], v3 = acc[i][j][e4 * 4 + 3];
+            *(uint2*)((TE*)p.out + (size_t)(m0 + wm + i * 32 + fr) * p.ldo + c) = make_uint2(
+                H16<TE>::pack2(v0 * gelu_tanh_grad_f(H16<TE>::lo(uu.x)), v1 * gelu_tanh_grad_f(H16<TE>::hi(uu.x))),
+                H16<TE>::pack2(v2 * gelu_tanh_grad_f(H16<TE>::lo(uu.y)), v3 * gelu_tanh_grad_f(H16<TE>::hi(uu.y))));
+          }
         }
+      } else {
+        // One body per bias source, picked by a uniform branch: a bias that
+        // could come from LDS or from global memory (or be a constant) at the
+        // same point makes the compiler wait on both counters there, and the
+        // vector-memory wait drains the stores.
+        auto full_epi = [&](auto bias_at) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int c = n0 + wn + j * 32 + e4 * 8 + g * 4;
+              const float4 b = bias_at(c);
+#pragma unroll
+              for (int i = 0; i < FM; ++i) {
+                const int r = m0 + wm + i * 32 + fr;
+                if constexpr (EPI == EPI_RESID) {  // the residual is already in acc
+                  *(float4*)((float*)p.out + (size_t)r * p.ldo + c) =
+                      make_float4(acc[i][j][e4 * 4 + 0] + b.x, acc[i][j][e4 * 4 + 1] + b.y,
+                                  acc[i][j][e4 * 4 + 2] + b.z, acc[i][j][e4 * 4 + 3] + b.w);
+                } else {
+                  epi_store4_full<EPI, TE>(p, r, c, b, acc[i][j][e4 * 4 + 0], acc[i][j][e4 * 4 + 1],
+                                           acc[i][j][e4 * 4 + 2], acc[i][j][e4 * 4 + 3]);
+                }
+              }
+            }
+        };
+        auto no_bias = [&](int) { return make_float4(0.f, 0.f, 0.f, 0.f); };
+        if constexpr (EPI_HAS_BIAS) {
+          if (lds_bias)
+            full_epi([&](int c) { return lds_read_bias4(bias_s + c); });
+          else if (p.bias != nullptr)
+            full_epi([&](int c) { return *(const float4*)(p.bias + c); });
+          else
+            full_epi(no_bias);
+        } else {
+          full_epi(no_bias);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i)

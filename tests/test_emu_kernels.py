@@ -102,6 +102,52 @@ def test_emu_nt_gemm_full_rows(L, N, K, epi):
         close(f64(out), acc * O.gelu_tanh_grad(f64(aux)), 2 ** -8, "gelu derivative")
 
 
+@pytest.mark.parametrize("M,N,K,epi,in_place", [
+    (4096, 4352, 64, EPI_GELU, False),   # bias wider than its LDS stage: the global-bias epilogue
+    (4096, 4100, 40, EPI_STORE, False),  # the same with a ragged last column of tiles
+    (4096, 768, 64, EPI_DGELU, False),   # gelu' on 256x192 tiles (its own prefetch depth)
+    (300, 768, 72, EPI_RESID, True),     # residual updated in place, full and ragged row tiles
+    (600, 700, 64, EPI_RESID, True),     # ragged rows and columns, in place
+])
+def test_emu_nt_gemm_epilogue_paths(L, M, N, K, epi, in_place):
+    """The NT epilogue's other paths: the bias read from global memory when
+    it does not fit its LDS stage, gelu' at the 256x192 tile, and the
+    residual added in place (the residual enters the accumulators of whole
+    tiles before their MFMAs; ragged tiles add it in the epilogue)."""
+    rng = np.random.default_rng(M + N + K + epi)
+    A = bf16(rng.standard_normal((M, K)))
+    B = bf16(rng.standard_normal((N, K)) * 0.1)
+    bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32))
+    acc = f64(A) @ f64(B).T
+    b = bias.double().numpy()
+    out2 = None
+    if epi == EPI_RESID:
+        x = rng.standard_normal((M, N)).astype(np.float32)
+        out = torch.from_numpy(x.copy())
+        aux = out if in_place else torch.from_numpy(x.copy())
+    elif epi == EPI_DGELU:
+        out = torch.zeros((M, N), dtype=torch.bfloat16)
+        aux = bf16(rng.standard_normal((M, N)))
+    else:
+        out = torch.zeros((M, N), dtype=torch.bfloat16)
+        aux = None
+        out2 = torch.zeros((M, N), dtype=torch.bfloat16) if epi == EPI_GELU else None
+    with_bias = epi in (EPI_STORE, EPI_GELU, EPI_RESID)
+    st = L.emu_gemm(M, N, K, ptr(A), K, 0, ptr(B), K, 0, epi, ptr(out), N,
+                    ptr(out2) if out2 is not None else None, ptr(aux) if aux is not None else None,
+                    ptr(bias) if with_bias else None, 1.0, 0.0, 1, None, 0)
+    assert st == 0
+    if epi == EPI_RESID:
+        close(out.double().numpy(), x.astype(np.float64) + acc + b, 1e-6, "residual")
+    elif epi == EPI_DGELU:
+        close(f64(out), acc * O.gelu_tanh_grad(f64(aux)), 2 ** -8, "gelu derivative")
+    elif epi == EPI_GELU:
+        close(f64(out), acc + b, 2 ** -8, "gelu pre-activation")
+        close(f64(out2), O.gelu_tanh(acc + b), 2 ** -8, "gelu")
+    else:
+        close(f64(out), acc + b, 2 ** -8, "store")
+
+
 @pytest.mark.parametrize("M,N,K,lda,epi", [
     (16384, 768, 96, 96, EPI_STORE),     # 256x192 tiles: the dX shapes with C outputs
     (16384, 3072, 64, 64, EPI_DGELU),    # 256x256 tiles: mproj dX with gelu'

@@ -145,3 +145,43 @@ def test_the_serialization_check_sees_one():
     assert serialized_loads(["global_load_dwordx4 v[0:3], v8, s[2:3]",
                              "global_load_dwordx4 v[4:7], v9, s[2:3]", "s_waitcnt vmcnt(1)",
                              "s_waitcnt vmcnt(0)"]) == 0
+
+
+def longest_store_run(instrs):
+    """The longest run of global stores with no full vector-memory wait
+    (vmcnt(0)) between them: a wait with a nonzero count leaves the later
+    stores and loads in flight, a full one drains every earlier store."""
+    best = run = 0
+    for t in instrs:
+        if t.startswith("global_store"):
+            run += 1
+            best = max(best, run)
+        elif re.match(r"s_waitcnt\b.*\bvmcnt\(0\)", t):
+            run = 0
+    return best
+
+
+@pytest.mark.parametrize("epi", [0, 2, 3, 4])
+def test_epilogues_stream_their_stores(disassembly, epi):
+    """The whole-tile epilogues (plain store with bias, GELU, residual,
+    gelu'; the 256x192 and 256x256 tiles) have a body that issues all of a
+    lane's stores with no full wait between them: the bias comes from LDS,
+    the residual is already in the accumulators, and gelu' prefetches its u
+    values several groups ahead.  Each bias, residual or u load had been
+    waited for with vmcnt(0), which also drained every store issued before
+    it (one to eight stores per wait)."""
+    ks = kernels(disassembly)
+    for tile, per_lane in (("Li256ELi192ELi2ELi2E", 48), ("Li256ELi256ELi4ELi2E", 32)):
+        name = [k for k in ks if re.search(rf"k_gemm_ntIDF16b{tile}Li{epi}ELb0E", k)]
+        assert len(name) == 1, (tile, epi)
+        want = per_lane * (2 if epi == 2 else 1)   # GELU writes u and gelu(u)
+        got = longest_store_run(ks[name[0]])
+        assert got >= want, (name[0], got, want)
+
+
+def test_the_store_run_check():
+    assert longest_store_run(["global_store_dwordx2 v[0:1], v[2:3], off", "s_waitcnt vmcnt(0)",
+                              "global_load_dwordx4 v[4:7], v[0:1], off", "global_store_dwordx2 v[0:1], v[2:3], off",
+                              "global_store_dwordx2 v[0:1], v[2:3], off"]) == 2
+    assert longest_store_run(["global_store_dwordx2 v[0:1], v[2:3], off", "s_waitcnt vmcnt(9)",
+                              "global_store_dwordx2 v[0:1], v[2:3], off"]) == 2
