@@ -135,10 +135,19 @@ __device__ __forceinline__ void attn_fwd_tile(const uint16_t* Ks, const uint16_t
   typedef typename H16<TE>::v8 v8;
   const int fr = lane & 31, g = lane >> 5;
   f32x16 s[2] = {zero16(), zero16()};
+  // All eight key fragments are read before the first MFMA, and the two
+  // 32-key blocks' MFMAs alternate: the reads' latency is paid once per
+  // tile instead of before every MFMA.
+  v8 kf[2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s[kb] = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s[kb]);
+    for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(kf[kb][ks], qf[ks], s[kb]);
   // Raw scores (masked ones -inf); the running max m_i is in log2 units.
   // It is raised only when the tile's max exceeds it by more than
   // RESCALE_LOG2: otherwise the tile's probabilities are taken against the
@@ -328,10 +337,24 @@ __device__ __forceinline__ void attn_dq_tile(const uint16_t* Ks, const uint16_t*
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f32x16 s = zero16(), dp = zero16();
+    // fragments read two k steps ahead of their MFMAs (all eight up front
+    // would cost this kernel its third wave per SIMD)
+    v8 kfr[4], vfr[4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      kfr[ks] = lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g);
+      vfr[ks] = lds_row<TE>(Vs, kb * 32 + fr, 2 * ks + g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      s = mfma(lds_row<TE>(Ks, kb * 32 + fr, 2 * ks + g), qf[ks], s);
-      dp = mfma(lds_row<TE>(Vs, kb * 32 + fr, 2 * ks + g), dof[ks], dp);
+      s = mfma(kfr[ks], qf[ks], s);
+      dp = mfma(vfr[ks], dof[ks], dp);
+      if (ks + 2 < 4) {
+        kfr[ks + 2] = lds_row<TE>(Ks, kb * 32 + fr, 2 * (ks + 2) + g);
+        vfr[ks + 2] = lds_row<TE>(Vs, kb * 32 + fr, 2 * (ks + 2) + g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (diag) {  // masked scores to -inf: their probability comes out as 0
 #pragma unroll
@@ -457,10 +480,18 @@ __device__ __forceinline__ void attn_dkv_tile(const uint16_t* Qs, const uint16_t
     // S and dP for 32 queries x this wave's 32 keys:
     // rows q = q0 + qb*32 + 8(e/4) + 4g + e%4, column key
     f32x16 s = zero16(), dp = zero16();
+    // the eight fragments first, then the MFMAs (as in the forward)
+    v8 qfr[4], ofr[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      s = mfma(lds_row<TE>(Qs, qb * 32 + fr, 2 * ks + g), kf[ks], s);
-      dp = mfma(lds_row<TE>(Os, qb * 32 + fr, 2 * ks + g), vf[ks], dp);
+      qfr[ks] = lds_row<TE>(Qs, qb * 32 + fr, 2 * ks + g);
+      ofr[ks] = lds_row<TE>(Os, qb * 32 + fr, 2 * ks + g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s = mfma(qfr[ks], kf[ks], s);
+      dp = mfma(ofr[ks], vf[ks], dp);
     }
     if (diag) {  // masked scores to -inf: their probability comes out as 0
 #pragma unroll
