@@ -53,6 +53,11 @@ def disassembly(tmp_path_factory):
 
 
 @pytest.fixture(scope="module")
+def disassembly_attention(tmp_path_factory):
+    return _disassemble("attention.hip", tmp_path_factory.mktemp("attention_isa"))
+
+
+@pytest.fixture(scope="module")
 def disassembly_elementwise(tmp_path_factory):
     return _disassemble("elementwise.hip", tmp_path_factory.mktemp("elementwise_isa"))
 
@@ -185,3 +190,32 @@ def test_the_store_run_check():
                               "global_store_dwordx2 v[0:1], v[2:3], off"]) == 2
     assert longest_store_run(["global_store_dwordx2 v[0:1], v[2:3], off", "s_waitcnt vmcnt(9)",
                               "global_store_dwordx2 v[0:1], v[2:3], off"]) == 2
+
+
+def reads_ahead(instrs):
+    """The most 16-byte LDS reads issued in a row before the next MFMA."""
+    best = run = 0
+    for t in instrs:
+        if t.startswith("ds_read_b128"):
+            run += 1
+            best = max(best, run)
+        elif t.startswith("v_mfma"):
+            run = 0
+    return best
+
+
+@pytest.mark.parametrize("kernel,ahead", [("k_attn_fwd64", 8), ("k_attn_dkv64", 8), ("k_attn_dq64", 4)])
+def test_attention_score_reads_run_ahead(disassembly_attention, kernel, ahead):
+    """The score phase (S = K Q^T, and dP in the backward) reads its key or
+    query fragments ahead of the MFMAs that use them: all eight in the
+    forward and dK/dV, two k steps (four reads) in dQ, which would lose its
+    third wave per SIMD otherwise.  The compiler had issued the forward's
+    reads at most two ahead of their MFMAs and dK/dV's at most six.  (For
+    dQ this bound does not separate the versions: its first four reads
+    were already issued together; the change is that later reads stay two
+    steps ahead instead of one.)"""
+    ks = kernels(disassembly_attention)
+    names = [k for k in ks if kernel in k and "IDF16" in k]
+    assert names, kernel
+    for k in names:
+        assert reads_ahead(ks[k]) >= ahead, (k, reads_ahead(ks[k]))
