@@ -122,13 +122,16 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
   const float invC = 1.0f / (float)C;
   for (; row < M; row += stride) {
     const bool more = row + stride < M;
+    // The next row's loads, issued before this row's reductions and without
+    // a branch around them (the last row reloads itself): loads under a
+    // branch leave a register copy at the join that waits for them, and the
+    // prefetch would then overlap nothing.
+    const int rn = more ? row + stride : row;
     float4 vn[NV];
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        int c = (lane + i * 64) * 4;
-        vn[i] = ln_in<FULL>(c, C) ? *(const float4*)(x + (size_t)(row + stride) * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+    for (int i = 0; i < NV; ++i) {
+      int c = (lane + i * 64) * 4;
+      vn[i] = ln_in<FULL>(c, C) ? *(const float4*)(x + (size_t)rn * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float s = 0.f;
 #pragma unroll
@@ -156,10 +159,8 @@ __global__ __launch_bounds__(256) void k_ln_fwd(const float* __restrict__ x,
       mean[row] = mu;
       rstd[row] = rs;
     }
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) v[i] = vn[i];
-    }
+    for (int i = 0; i < NV; ++i) v[i] = vn[i];
   }
 }
 
@@ -200,13 +201,16 @@ int ln_bwd_blocks(int M) {
   return nb < 512 ? nb : 512;
 }
 
-template <typename TA, int NV, bool FULL>
+// ACC: add to the residual gradient already in dres (a template parameter:
+// as a run-time flag, the compiler sank part of that load into the branch
+// that uses it, where its wait drained the next row's prefetch).
+template <typename TA, int NV, bool FULL, bool ACC>
 __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
                                                 const float* __restrict__ mean,
                                                 const float* __restrict__ rstd,
                                                 const float* __restrict__ w,
                                                 const TA* __restrict__ dy, float* __restrict__ dres,
-                                                TA* __restrict__ dres_act, int accum,
+                                                TA* __restrict__ dres_act,
                                                 float* __restrict__ part, int M, int C, int rpb) {
   __shared__ float red[2][4][1024];
   int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -246,11 +250,14 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
     float4 xn[NV];
     Raw dn[NV];
     float mun = 0.f, rsn = 0.f;
-    if (more) load_row(row + 4, xn, dn, mun, rsn);
+    // Unconditional, as in the forward (the last row reloads itself): loads
+    // under a branch are waited for where the paths join, before this row's
+    // reductions.
+    load_row(more ? row + 4 : row, xn, dn, mun, rsn);
     float* dr = dres + (size_t)row * C;
     TA* da = dres_act + (size_t)row * C;
     float4 prev[NV];
-    if (accum) {
+    if constexpr (ACC) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         int c = (lane + i * 64) * 4;
@@ -281,22 +288,20 @@ __global__ __launch_bounds__(256) void k_ln_bwd(const float* __restrict__ x,
       if (ln_in<FULL>(c, C)) {
         float4 o = make_float4(rs * (gg[i].x - mg - xh[i].x * mgx), rs * (gg[i].y - mg - xh[i].y * mgx),
                                rs * (gg[i].z - mg - xh[i].z * mgx), rs * (gg[i].w - mg - xh[i].w * mgx));
-        if (accum) {
+        if constexpr (ACC) {
           o.x += prev[i].x; o.y += prev[i].y; o.z += prev[i].z; o.w += prev[i].w;
         }
         *(float4*)(dr + c) = o;
         Vec4<TA>::store(da + c, o.x, o.y, o.z, o.w);
       }
     }
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        xc[i] = xn[i];
-        dc[i] = dn[i];
-      }
-      mu = mun;
-      rs = rsn;
+    for (int i = 0; i < NV; ++i) {
+      xc[i] = xn[i];
+      dc[i] = dn[i];
     }
+    mu = mun;
+    rs = rsn;
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -319,8 +324,12 @@ template <typename TA, int NV, bool FULL>
 static void ln_bwd_launch(int nb, hipStream_t st, const float* x, const float* mean, const float* rstd,
                           const float* w, const void* dy, float* dres, void* dres_act, bool accum, float* part,
                           int M, int C, int rpb) {
-  k_ln_bwd<TA, NV, FULL><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const TA*)dy, dres, (TA*)dres_act, accum, part,
-                                             M, C, rpb);
+  if (accum)
+    k_ln_bwd<TA, NV, FULL, true><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const TA*)dy, dres, (TA*)dres_act,
+                                                     part, M, C, rpb);
+  else
+    k_ln_bwd<TA, NV, FULL, false><<<nb, 256, 0, st>>>(x, mean, rstd, w, (const TA*)dy, dres, (TA*)dres_act,
+                                                      part, M, C, rpb);
 }
 template <typename TA>
 static void ln_bwd_width(int nb, hipStream_t st, const float* x, const float* mean, const float* rstd,

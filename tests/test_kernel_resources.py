@@ -28,7 +28,7 @@ FLOORS = [
     ("k_ln_fwdIDF16bLi4E", 4, "its grid puts four waves on every SIMD"),
     ("k_ln_bwdIDF16bLi4E", 2, "its grid puts two waves on every SIMD"),
     ("k_ln_fwdIDF16bLi3ELb1E", 4, "the 768-wide variant of the 124M model"),
-    ("k_ln_bwdIDF16bLi3ELb1E", 3, "the 768-wide variant: no column tests, 131 registers"),
+    ("k_ln_bwdIDF16bLi3ELb1E", 4, "the 768-wide variant: no column tests, unconditional prefetch, 128 registers"),
     ("k_gemm_ntIDF16bLi256ELi256E", 2, "two waves per SIMD at the 256x256 tile"),
     ("k_gemm_tnIDF16bLi256ELi256E", 2, ""),
     ("k_gemm_ntIDF16bLi256ELi192E", 1, ""),
