@@ -1166,6 +1166,20 @@ struct F32Loader {
       r[i] = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
+  // The whole 128 x 16 tile in bounds and 16-byte aligned: plain loads, no
+  // tests (a test around each load left a register copy where its paths
+  // joined, and that copy waited for the load, so the next stage's loads
+  // no longer overlapped the current stage's MFMAs).
+  __device__ __forceinline__ void load_whole(const float* __restrict__ base, long ld, int row0, int k0,
+                                             int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      const int row = TRANS ? (c & 31) * 4 : c >> 2, k = TRANS ? c >> 5 : (c & 3) * 4;
+      r[i] = TRANS ? *(const float4*)(base + (size_t)(k0 + k) * ld + row0 + row)
+                   : *(const float4*)(base + (size_t)(row0 + row) * ld + k0 + k);
+    }
+  }
   __device__ __forceinline__ void store(float* __restrict__ lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -1185,7 +1199,7 @@ struct F32Loader {
 };
 
 template <bool AT, bool BT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_f32m(GP p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_f32m(GP p) {
   __shared__ float As[2][F32M_BK * F32M_LD], Bs[2][F32M_BK * F32M_LD];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m0 = blockIdx.y * F32M_BM, n0 = blockIdx.x * F32M_BM;
@@ -1205,20 +1219,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(GP p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
-    lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool nxt = kt + 1 < nk;
-    if (nxt) {
-      la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * F32M_BK, kend, tid);
-      lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * F32M_BK, kend, tid);
-    }
+  auto mfma_stage = [&](int cur) {
 #pragma unroll
     for (int ks = 0; ks < F32M_BK; ks += 2) {
       const float* ar = As[cur] + (ks + fk) * F32M_LD;
@@ -1230,20 +1231,118 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(GP p) {
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
-    if (nxt) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+  };
+  // uniform per block: every stage of this tile is whole and aligned
+  const bool whole = m0 + F32M_BM <= p.M && n0 + F32M_BM <= p.N && (kend - kbeg) % F32M_BK == 0 &&
+                     (p.lda & 3) == 0 && (p.ldb & 3) == 0;
+  if (whole) {
+    // The next stage's loads, with no branch around them (the last stage
+    // reloads itself), are in flight during this stage's MFMAs.
+    if (nk > 0) {
+      la.load_whole(A, p.lda, m0, kbeg, tid);
+      lb.load_whole(B, p.ldb, n0, kbeg, tid);
+      la.store(As[0], tid);
+      lb.store(Bs[0], tid);
     }
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const int kn = kbeg + (kt + 1 < nk ? kt + 1 : kt) * F32M_BK;
+      la.load_whole(A, p.lda, m0, kn, tid);
+      lb.load_whole(B, p.ldb, n0, kn, tid);
+      sched_fence();  // keep the loads ahead of the MFMAs
+      mfma_stage(cur);
+      la.store(As[cur ^ 1], tid);  // unused after the last stage
+      lb.store(Bs[cur ^ 1], tid);
+      __syncthreads();
+    }
+  } else {
+    if (nk > 0) {
+      la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
+      lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
+      la.store(As[0], tid);
+      lb.store(Bs[0], tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool nxt = kt + 1 < nk;
+      if (nxt) {
+        la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * F32M_BK, kend, tid);
+        lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * F32M_BK, kend, tid);
+      }
+      mfma_stage(cur);
+      if (nxt) {
+        la.store(As[cur ^ 1], tid);
+        lb.store(Bs[cur ^ 1], tid);
+      }
+      __syncthreads();
+    }
   }
+  if (m0 + F32M_BM <= p.M && n0 + F32M_BM <= p.N) {
+    // A whole tile: the lane's two bias values first, then per fragment its
+    // 16 inputs (residual, u, or the accumulated gradient) loaded together
+    // before its 16 stores; one element at a time, each load's wait had
+    // also drained every store before it.
+    float bj[2] = {0.f, 0.f};
+    if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
+      if (p.bias != nullptr) {
+        bj[0] = p.bias[n0 + wn + fr];
+        bj[1] = p.bias[n0 + wn + 32 + fr];
+      }
+    }
+    constexpr bool LOADS = EPI == EPI_RESID || EPI == EPI_DGELU || EPI == EPI_WGRAD;
+    float* wout = (float*)p.out + (EPI == EPI_WGRAD ? (size_t)blockIdx.z * ((size_t)p.M * p.ldo) : 0);
+    const bool wg_acc = EPI == EPI_WGRAD && gridDim.z == 1 && p.beta != 0.f;  // uniform
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        const int c = n0 + wn + j * 32 + fr;
+        // one 64-bit base per fragment, 32-bit row offsets (rows 8 (e/4) +
+        // e%4 below the fragment's first row of this lane)
+        const size_t o0 = (size_t)(m0 + wm + i * 32 + 4 * fk) * p.ldo + c;
+        const int ld = (int)p.ldo;
+        float in[16];
+        if constexpr (LOADS) {
+          if (EPI != EPI_WGRAD || wg_acc) {
+            const float* src = (EPI == EPI_WGRAD ? (const float*)wout : (const float*)p.aux) + o0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        epi_store<EPI, float>(p, m0 + wm + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3), n0 + wn + j * 32 + fr,
-                              acc[i][j][e]);
+            for (int e = 0; e < 16; ++e) in[e] = src[(8 * (e >> 2) + (e & 3)) * ld];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const size_t o = o0 + (size_t)((8 * (e >> 2) + (e & 3)) * ld);
+          const float a = acc[i][j][e];
+          if constexpr (EPI == EPI_STORE) {
+            ((float*)p.out)[o] = p.alpha * a + bj[j];
+          } else if constexpr (EPI == EPI_LOGITS) {
+            ((float*)p.out)[o] = a;
+          } else if constexpr (EPI == EPI_GELU) {
+            const float u = a + bj[j];
+            ((float*)p.out)[o] = u;
+            ((float*)p.out2)[o] = gelu_tanh_f(u);
+          } else if constexpr (EPI == EPI_RESID) {
+            ((float*)p.out)[o] = in[e] + a + bj[j];
+          } else if constexpr (EPI == EPI_DGELU) {
+            ((float*)p.out)[o] = a * gelu_tanh_grad_f(in[e]);
+          } else {  // EPI_WGRAD: raw partials with split-K
+            if (gridDim.z > 1) wout[o] = a;
+            else wout[o] = wg_acc ? p.alpha * a + p.beta * in[e] : p.alpha * a;
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          epi_store<EPI, float>(p, m0 + wm + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3), n0 + wn + j * 32 + fr,
+                                acc[i][j][e]);
+  }
 }
 
 // ------------------------------------------------------------------ split-K reduction

@@ -487,6 +487,9 @@ def test_emu_attention_forward_rising_scores(L):
     (600, 320, 768, 0, 1, EPI_DGELU),     # dX layout (B transposed in memory)
     (768, 768, 4096, 1, 1, EPI_WGRAD),    # weight gradient: 7 K splits + reduction
     (300, 452, 1100, 1, 1, EPI_WGRAD),    # ragged weight gradient, accumulate
+    (512, 384, 768, 0, 0, EPI_STORE),     # whole tiles: the untested loads and epilogue
+    (512, 256, 1024, 0, 0, EPI_GELU),
+    (1024, 1024, 128, 1, 1, EPI_WGRAD),   # whole tiles, no split, accumulate
 ])
 def test_emu_fp32_mfma_gemm(L, M, N, K, at, bt, epi):
     """fp32 problems of 2^27 multiply-adds or more run on the fp32 matrix
@@ -501,7 +504,7 @@ def test_emu_fp32_mfma_gemm(L, M, N, K, at, bt, epi):
     out0 = rng.standard_normal((M, N)).astype(np.float32)
     out = out0.copy()
     out2 = np.zeros((M, N), np.float32)
-    alpha, beta = (0.5, 1.0) if (epi == EPI_WGRAD and M == 300) else (1.0, 0.0)
+    alpha, beta = (0.5, 1.0) if (epi == EPI_WGRAD and M in (300, 1024)) else (1.0, 0.0)
     ws_n = L.emu_gemm_splitk_ws_elems(M, N, 16384)
     ws = np.zeros(max(ws_n, 1), np.float32)
     st = L.emu_gemm(M, N, K, ptr(A), M if at else K, at, ptr(B), N if bt else K, bt, epi, ptr(out), N,
