@@ -47,25 +47,46 @@ __global__ __launch_bounds__(256) void k_attn_decode(const TA* __restrict__ qkv,
   __shared__ float red_o[4][128];
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int C = H * hd;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index through readfirstlane: uniform to the compiler, so the
+  // key loop below stays a scalar loop
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const TA* qrow = qkv + (size_t)b * 3 * C + h * hd;
   const float q0 = lane < hd ? to_f(qrow[lane]) : 0.f;
   const float q1 = lane + 64 < hd ? to_f(qrow[lane + 64]) : 0.f;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   const TA* kb = cache + (size_t)b * Tmax * 2 * C + h * hd;
-  for (int j = w; j < nkeys; j += 4) {
-    const TA* kr = kb + (size_t)j * 2 * C;
-    const TA* vr = kr + C;
-    float s = 0.f;
-    if (lane < hd) s = q0 * to_f(kr[lane]);
-    if (lane + 64 < hd) s += q1 * to_f(kr[lane + 64]);
-    s = wave_sum(s) * sl2;
+  // Each wave's keys j = w, w + 4, ...: the next key's K and V elements are
+  // loaded before this key's reduction, so one load latency per key
+  // overlaps the previous key's work instead of adding to it.  The loads
+  // carry no lane test (a lane past hd reads element 0, whose product with
+  // q = 0 adds nothing, and whose output slot is never read): loads under
+  // a test are waited for where the paths join.
+  // Two register sets alternate (keys j and j + 4), so the loop carries no
+  // copy of a loaded register, which would wait for its load.
+  const int i0 = lane < hd ? lane : 0, i1 = lane + 64 < hd ? lane + 64 : 0;
+  struct KV { float k0, k1, v0, v1; };
+  auto load_key = [&](int j) {
+    const TA* kr = kb + (size_t)(j < nkeys ? j : nkeys - 1) * 2 * C;  // past the last key: reload it
+    return KV{to_f(kr[i0]), to_f(kr[i1]), to_f(kr[C + i0]), to_f(kr[C + i1])};
+  };
+  auto use_key = [&](const KV& kv) {
+    const float s = wave_sum(q0 * kv.k0 + q1 * kv.k1) * sl2;
     const float mn = fmaxf(m, s);
     const float a = __builtin_amdgcn_exp2f(m - mn), p = __builtin_amdgcn_exp2f(s - mn);
     l = l * a + p;
-    o0 = o0 * a + (lane < hd ? p * to_f(vr[lane]) : 0.f);
-    o1 = o1 * a + (lane + 64 < hd ? p * to_f(vr[lane + 64]) : 0.f);
+    o0 = o0 * a + p * kv.v0;
+    o1 = o1 * a + p * kv.v1;
     m = mn;
+  };
+  KV ka = load_key(w);
+  for (int j = w; j < nkeys; j += 8) {
+    const KV kb2 = load_key(j + 4);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the use
+    use_key(ka);
+    if (j + 4 >= nkeys) break;
+    ka = load_key(j + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    use_key(kb2);
   }
   if (lane == 0) {
     red_m[w] = m;
